@@ -1,0 +1,155 @@
+"""The lm_head verify pass: argmax per row, near-tie classification and the
+greedy accept-prefix length.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What is computed
+----------------
+Logits l[m, v] are the NVFP4 GEMM of ``oracle.nvfp4`` with N = V rows.
+Row m's token is argmax_v l[m, v]; among equal maxima the LOWEST index wins
+(the numpy/torch argmax convention; the pages do not say).
+
+Speculative verify (TandemLLM README, introduction and "Architecture: the
+parts"): drafters propose tokens, the target checks them all in one pass,
+the longest prefix the target agrees with is kept, and at the first wrong
+guess the target's own token is emitted instead.  With T rows per sequence
+and drafts d[0..T-2], row j's argmax is the target's choice for the
+position that draft d[j] fills, so
+
+    accept_len = the largest L <= T-1 with d[j] == argmax[j] for all j < L.
+
+The emitted bonus token is argmax[accept_len]; it is not a separate output.
+A batch of M = S*T rows holds S independent sequences in contiguous blocks
+of T rows (ling-engine README, "Six levers": several sequences share one
+weight read).
+
+Exactness limit: the pages concede that a batched verify may round the
+other way where the top two logits are within an ulp (TandemLLM README,
+introduction).  A row is *decisive* iff the oracle's top-2 gap exceeds the
+acceptance bound of both contenders; only decisive rows (and steps whose
+compared rows are all decisive) must match exactly.  The stricter
+interval-overlap test is available with ``interval=True``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .nvfp4 import bf16_bits_to_f64, dequant, tolerance_bound
+
+
+def top2_merge(v1, i1, v2, i2, c1, j1, c2, j2):
+    """Merge a running (best, second) per row with a new chunk's (best,
+    second), where every index of the chunk is larger than every index seen
+    so far (chunks are visited in increasing index order).  Order is value
+    descending, then index ascending, so on equal values the running
+    entries win.  All arguments are arrays over rows."""
+    take_c1 = c1 > v1
+    nv1 = np.where(take_c1, c1, v1)
+    ni1 = np.where(take_c1, j1, i1)
+    # Candidates for second place: if the chunk's best took first place,
+    # the old best (lower index) against the chunk's second; otherwise the
+    # old second (lower index) against the chunk's best.
+    a_v = np.where(take_c1, v1, v2)
+    a_i = np.where(take_c1, i1, i2)
+    b_v = np.where(take_c1, c2, c1)
+    b_i = np.where(take_c1, j2, j1)
+    take_b = b_v > a_v
+    return nv1, ni1, np.where(take_b, b_v, a_v), np.where(take_b, b_i, a_i)
+
+
+def _chunk_top2(logits: np.ndarray, base: int):
+    """Best and second-best (value, global index) per row of one chunk;
+    first occurrence wins among equal values."""
+    rows = np.arange(logits.shape[0])
+    a1 = np.argmax(logits, axis=1)
+    v1 = logits[rows, a1]
+    if logits.shape[1] < 2:
+        return v1, a1 + base, np.full_like(v1, -np.inf), np.full_like(a1, -1)
+    masked = logits.copy()
+    masked[rows, a1] = -np.inf
+    a2 = np.argmax(masked, axis=1)
+    return v1, a1 + base, masked[rows, a2], a2 + base
+
+
+def accept_len_ref(drafts: np.ndarray, argmax: np.ndarray) -> int:
+    """Greedy accept: the number of leading positions where the draft equals
+    the target's argmax.  drafts has T-1 entries, argmax has T."""
+    drafts = np.asarray(drafts).reshape(-1)
+    argmax = np.asarray(argmax).reshape(-1)
+    if drafts.shape[0] != argmax.shape[0] - 1:
+        raise ValueError("need T-1 drafts for T argmax rows")
+    length = 0
+    while length < drafts.shape[0] and int(drafts[length]) == int(argmax[length]):
+        length += 1
+    return length
+
+
+def _row_bound(ax_row: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float, v: int) -> float:
+    """Acceptance bound of logit (row, v): one dot product of |x| and |w_v|."""
+    w = dequant(wq[v:v + 1], ws[v:v + 1], g)[0]
+    return float(tolerance_bound(np.dot(ax_row, np.abs(w))))
+
+
+def lmhead_ref(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float,
+               T: int, drafts: np.ndarray | None = None, *,
+               interval: bool = False, row_chunk: int = 4096) -> dict:
+    """Run the lm_head verify pass on the CPU.
+
+    x_bits uint16[M][K] (bf16 bits), wq uint8[V][K/2], ws uint8[V][K/16],
+    g the tensor scale (part of every logit).  M must be a multiple of T;
+    drafts int[M/T][T-1] or None (then no accept lengths are computed).
+
+    Returns a dict with per-row ``argmax`` (int32), ``top1``/``top2`` logits,
+    ``idx2``, the bounds ``b1``/``b2`` of the two contenders and
+    ``decisive`` (gap > max(b1, b2)); with drafts, per-sequence
+    ``accept_len`` (int32) and ``step_decisive`` (every row the accept
+    decision reads, 0..min(L, T-2), is decisive); with ``interval=True``
+    also ``interval_decisive`` (l_top1 - b1 > max over v != top1 of l_v + b_v).
+    """
+    x = bf16_bits_to_f64(x_bits)
+    m, _k = x.shape
+    if T < 1 or m % T:
+        raise ValueError("M must be a positive multiple of T")
+    wq = np.asarray(wq, dtype=np.uint8)
+    ws = np.asarray(ws, dtype=np.uint8)
+    nv = wq.shape[0]
+    v1 = np.full(m, -np.inf); i1 = np.full(m, -1, dtype=np.int64)
+    v2 = np.full(m, -np.inf); i2 = np.full(m, -1, dtype=np.int64)
+    for r0 in range(0, nv, row_chunk):
+        r1 = min(nv, r0 + row_chunk)
+        logits = x @ dequant(wq[r0:r1], ws[r0:r1], g).T
+        v1, i1, v2, i2 = top2_merge(v1, i1, v2, i2, *_chunk_top2(logits, r0))
+    ax = np.abs(x)
+    b1 = np.array([_row_bound(ax[r], wq, ws, g, int(i1[r])) for r in range(m)])
+    b2 = np.array([_row_bound(ax[r], wq, ws, g, int(i2[r])) if i2[r] >= 0 else 0.0
+                   for r in range(m)])
+    out = {
+        "argmax": i1.astype(np.int32),
+        "top1": v1, "top2": v2, "idx2": i2.astype(np.int32),
+        "b1": b1, "b2": b2,
+        "decisive": (v1 - v2) > np.maximum(b1, b2),
+    }
+    if interval:
+        hi_other = np.full(m, -np.inf)
+        rows = np.arange(m)
+        for r0 in range(0, nv, row_chunk):
+            r1 = min(nv, r0 + row_chunk)
+            w = dequant(wq[r0:r1], ws[r0:r1], g)
+            hi = x @ w.T + tolerance_bound(ax @ np.abs(w).T)
+            inside = (i1 >= r0) & (i1 < r1)
+            hi[rows[inside], i1[inside] - r0] = -np.inf
+            hi_other = np.maximum(hi_other, hi.max(axis=1))
+        out["interval_decisive"] = (v1 - b1) > hi_other
+    if drafts is not None:
+        s = m // T
+        d = np.asarray(drafts, dtype=np.int64).reshape(s, T - 1)
+        acc = np.empty(s, dtype=np.int32)
+        step_dec = np.empty(s, dtype=bool)
+        for q in range(s):
+            rows_q = slice(q * T, (q + 1) * T)
+            acc[q] = accept_len_ref(d[q], out["argmax"][rows_q])
+            last = min(int(acc[q]), T - 2)
+            step_dec[q] = bool(np.all(out["decisive"][q * T:q * T + last + 1]))
+        out["accept_len"] = acc
+        out["step_decisive"] = step_dec
+    return out
