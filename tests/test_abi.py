@@ -1,0 +1,138 @@
+"""The C-ABI library loads without a GPU, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (CPU only).
+
+The pointers passed here are host addresses that are never dereferenced:
+every call below fails validation, which happens before the library
+touches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from verify_gemm_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+VG_OK, VG_ERR_NULL, VG_ERR_SHAPE, VG_ERR_UNSUPPORTED = 0, -1, -2, -3
+VG_ERR_HIP, VG_ERR_WORKSPACE, VG_ERR_ALIGN = -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from verify_gemm_amd import build
+        build.build()
+    return binding.load()
+
+
+@pytest.fixture(scope="module")
+def buf():
+    # 64-byte aligned host scratch used only as non-null pointer values
+    raw = np.zeros(4096 + 64, dtype=np.uint8)
+    base = raw.ctypes.data
+    off = (-base) % 64
+    return raw, base + off
+
+
+def test_exports_every_header_symbol(lib):
+    names = binding.header_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.vg_abi_version() == int(re.search(r"#define VG_ABI_VERSION (\d+)",
+                                                 open(binding.HEADER).read()).group(1))
+
+
+def test_status_strings(lib):
+    for code in (VG_OK, VG_ERR_NULL, VG_ERR_SHAPE, VG_ERR_UNSUPPORTED, VG_ERR_HIP, VG_ERR_WORKSPACE,
+                 VG_ERR_ALIGN):
+        assert binding.status_string(code) != "unknown status"
+    assert binding.status_string(12345) == "unknown status"
+
+
+def test_gemm_null_pointers(lib, buf):
+    _, p = buf
+    for args in [(None, p, p, p), (p, None, p, p), (p, p, None, p), (p, p, p, None)]:
+        x, wq, ws, y = args
+        assert lib.nvfp4_gemm(x, wq, ws, 1.0, 1, 16, 16, y, None) == VG_ERR_NULL
+        assert lib.nvfp4_gemm_ex(x, wq, ws, 1.0, 1, 16, 16, y, None, 0, None) == VG_ERR_NULL
+
+
+@pytest.mark.parametrize("m,n,k,code", [
+    (0, 16, 16, VG_ERR_SHAPE), (-1, 16, 16, VG_ERR_SHAPE), (1, 0, 16, VG_ERR_SHAPE),
+    (1, 16, 0, VG_ERR_SHAPE), (1, 16, 8, VG_ERR_SHAPE), (1, 16, 24, VG_ERR_SHAPE),
+    (1, 16, 17, VG_ERR_SHAPE), (69, 16, 16, VG_ERR_UNSUPPORTED), (1000, 16, 16, VG_ERR_UNSUPPORTED),
+])
+def test_gemm_bad_shapes(lib, buf, m, n, k, code):
+    _, p = buf
+    assert lib.nvfp4_gemm(p, p, p, 1.0, m, n, k, p, None) == code
+    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, m, n, k, p, p, 1 << 30, None) == code
+
+
+def test_gemm_misaligned(lib, buf):
+    _, p = buf
+    for x, wq, ws in [(p + 2, p, p), (p, p + 4, p), (p, p, p + 1)]:
+        assert lib.nvfp4_gemm(x, wq, ws, 1.0, 1, 16, 16, p, None) == VG_ERR_ALIGN
+
+
+def test_gemm_ex_workspace_checked(lib, buf):
+    _, p = buf
+    need = lib.vg_gemm_workspace_bytes(17, 5120, 5120)
+    assert need > 0
+    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 5120, p, None, 0, None) == VG_ERR_WORKSPACE
+    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 5120, p, p, need - 1, None) == VG_ERR_WORKSPACE
+
+
+def test_workspace_sizes(lib):
+    assert lib.vg_gemm_workspace_bytes(1, 5120, 5120) == 0          # M = 1 never splits K
+    assert lib.vg_gemm_workspace_bytes(0, 5120, 5120) == 0
+    assert lib.vg_gemm_workspace_bytes(69, 5120, 5120) == 0
+    assert lib.vg_gemm_workspace_bytes(17, 5120, 23) == 0
+    small = lib.vg_gemm_workspace_bytes(17, 5120, 5120)
+    big = lib.vg_gemm_workspace_bytes(68, 5120, 5120)
+    assert 0 < small < big
+    assert lib.vg_lmhead_workspace_bytes(17) >= 8 * 68
+    assert lib.vg_lmhead_workspace_bytes(0) == 0 and lib.vg_lmhead_workspace_bytes(69) == 0
+
+
+def test_lmhead_validation(lib, buf):
+    _, p = buf
+    f = lib.lmhead_argmax_accept
+    assert f(None, p, p, p, 17, 100, p, p, None) == VG_ERR_NULL
+    assert f(p, p, p, None, 17, 100, p, p, None) == VG_ERR_NULL      # drafts needed when M > 1
+    assert f(p, p, p, p, 17, 0, p, p, None) == VG_ERR_SHAPE
+    assert f(p, p, p, p, 0, 100, p, p, None) == VG_ERR_SHAPE
+    assert f(p, p, p, p, 69, 100, p, p, None) == VG_ERR_UNSUPPORTED
+    assert f(p + 2, p, p, p, 17, 100, p, p, None) == VG_ERR_ALIGN
+    g = lib.lmhead_argmax_accept_ex
+    ws = lib.vg_lmhead_workspace_bytes(17)
+    assert g(p, p, p, 1.0, p, 17, 5120, 100, 5, p, p, p, ws, None) == VG_ERR_SHAPE   # M % T
+    assert g(p, p, p, 1.0, p, 17, 5120, 100, 18, p, p, p, ws, None) == VG_ERR_SHAPE  # T > M
+    assert g(p, p, p, 1.0, p, 17, 5120, 100, 0, p, p, p, ws, None) == VG_ERR_SHAPE
+    assert g(p, p, p, 1.0, p, 17, 40, 100, 17, p, p, p, ws, None) == VG_ERR_SHAPE    # K % 16
+    assert g(p, p, p, 1.0, p, 17, 5120, 100, 17, p, p, None, ws, None) == VG_ERR_WORKSPACE
+    assert g(p, p, p, 1.0, p, 17, 5120, 100, 17, p, p, p, ws - 1, None) == VG_ERR_WORKSPACE
+    assert g(p, p, p, 1.0, None, 17, 5120, 100, 17, p, p, p, ws, None) == VG_ERR_NULL
+
+
+def test_bwprobe_validation(lib, buf):
+    _, p = buf
+    assert lib.vg_bwprobe(None, 1024, p, None) == VG_ERR_NULL
+    assert lib.vg_bwprobe(p, 1024, None, None) == VG_ERR_NULL
+    assert lib.vg_bwprobe(p, 0, p, None) == VG_ERR_SHAPE
+    assert lib.vg_bwprobe(p, 1000, p, None) == VG_ERR_ALIGN
+    assert lib.vg_bwprobe(p + 8, 1024, p, None) == VG_ERR_ALIGN
+    assert lib.vg_bwprobe_sink_floats() >= 256
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    saved = binding._lib
+    try:
+        binding._lib = None
+        with pytest.raises(ImportError):
+            binding.load(str(tmp_path / "missing.so"))
+    finally:
+        binding._lib = saved

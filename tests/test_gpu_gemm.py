@@ -1,0 +1,148 @@
+"""GPU parity of nvfp4_gemm against the CPU oracle (needs an MI355X).
+
+Every comparison is element by element against the oracle's fp64 result
+with the acceptance bound |y - y_ref| <= 1e-3 * sum_k |x_k w_k| + 1e-6."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev_bf16, dev_u8, guarded_output, guards_intact, within_bound
+from verify_gemm_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gemm(x_bits, wq, ws, g, *, workspace=None):
+    m, k = x_bits.shape
+    n = wq.shape[0]
+    y, buf, pad = guarded_output((m, n))
+    ws_t = None
+    if workspace:
+        ws_t = binding.new_workspace(binding.gemm_workspace_bytes(m, n, k))
+    binding.nvfp4_gemm(dev_bf16(x_bits), dev_u8(wq), dev_u8(ws), g, y, workspace=ws_t)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, pad), "write outside Y"
+    return y.cpu().numpy()
+
+
+def check(x_bits, wq, ws, g, label, workspace=False):
+    print(f"[case] {label} M={x_bits.shape[0]} N={wq.shape[0]} K={x_bits.shape[1]}", flush=True)
+    y = run_gemm(x_bits, wq, ws, g, workspace=workspace)
+    y_ref, bound = oracle.nvfp4_gemm_ref(x_bits, wq, ws, g)
+    ok, worst, at = within_bound(y, y_ref, bound)
+    assert ok, f"{label}: worst err/bound {worst:.3g} at {at}: gpu {y[at]} ref {y_ref[at]}"
+    return y
+
+
+def test_tiny_gemv_1024():
+    c = synth.tiny_gemv()
+    check(c["x"], c["wq"], c["ws"], c["g"], "tiny gemv")
+
+
+@pytest.mark.parametrize("n,k", [(17408, 5120), (5120, 5120)])
+def test_decode_gemv_shapes(n, k):
+    c = synth.decode_gemv(n, k)
+    check(c["x"], c["wq"], c["ws"], c["g"], "decode gemv")
+
+
+@pytest.mark.parametrize("n,k", [(5120, 17408), (17408, 5120)])
+def test_verify_gemm_shapes(n, k):
+    c = synth.verify_gemm(n, k)
+    check(c["x"], c["wq"], c["ws"], c["g"], "verify gemm")
+    check(c["x"], c["wq"], c["ws"], c["g"], "verify gemm (caller workspace)", workspace=True)
+
+
+def test_down_proj_m68():
+    c = synth.verify_gemm(5120, 17408, m=68)
+    check(c["x"], c["wq"], c["ws"], c["g"], "down M=68")
+
+
+@pytest.mark.parametrize("m", list(range(1, 69)))
+def test_every_m(m):
+    rng = np.random.default_rng(5000 + m)
+    n, k = 200, 2048                      # N not a multiple of any tile; several K windows
+    wq, ws = synth.gen_weights(rng, n, k)
+    x = synth.gen_x(rng, m, k)
+    check(x, wq, ws, 1.25, "every M")
+
+
+@pytest.mark.parametrize("m", [1, 2, 16, 17, 33, 68])
+@pytest.mark.parametrize("n,k", [(1, 16), (7, 48), (65, 272), (130, 1040), (64, 1056), (3, 5136)])
+def test_k_and_n_tails(m, n, k):
+    rng = np.random.default_rng(7000 + m * 31 + n * 7 + k)
+    wq, ws = synth.gen_weights(rng, n, k)
+    x = synth.gen_x(rng, m, k)
+    check(x, wq, ws, 0.75, "tails")
+
+
+@pytest.mark.parametrize("m", [1, 17])
+def test_all_finite_scale_codes_and_signs(m):
+    rng = np.random.default_rng(8000 + m)
+    n, k = 254, 4096
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    wq = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    ws = np.resize(finite, (n, k // 16)).astype(np.uint8)       # every code, negative and subnormal
+    ws = ws[:, rng.permutation(k // 16)]
+    x = synth.gen_x(rng, m, k)
+    check(x, wq, ws, 1.5, "all scale codes")
+
+
+@pytest.mark.parametrize("m", [1, 4, 17, 68])
+def test_zero_blocks_and_zero_scales(m):
+    rng = np.random.default_rng(9000 + m)
+    n, k = 128, 1024
+    wq, ws = synth.gen_weights(rng, n, k)
+    wq[:, :64] = 0x00            # +0 codes
+    wq[:, 64:128] = 0x88         # -0 codes
+    ws[:, 20:30] = 0x00          # zero scale
+    ws[:, 30:32] = 0x80          # -0 scale
+    wq[5] = 0
+    x = synth.gen_x(rng, m, k)
+    y = check(x, wq, ws, 1.0, "zero blocks")
+    assert np.all(y[:, 5] == 0)
+
+
+@pytest.mark.parametrize("m", [1, 17, 68])
+def test_wide_dynamic_range_x(m):
+    rng = np.random.default_rng(9100 + m)
+    n, k = 96, 2048
+    wq, ws = synth.gen_weights(rng, n, k)
+    mag = np.exp2(rng.integers(-60, 61, (m, k))).astype(np.float32)
+    sign = np.where(rng.random((m, k)) < 0.5, -1.0, 1.0).astype(np.float32)
+    x = synth.f32_to_bf16_bits(mag * sign * (1 + rng.integers(0, 128, (m, k)) / 128).astype(np.float32))
+    check(x, wq, ws, 1.0, "wide range X")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 17408, 5120), (17, 5120, 5120), (68, 5120, 17408)])
+def test_bitwise_repeatable(m, n, k):
+    rng = np.random.default_rng(9200 + m)
+    wq, ws = synth.gen_weights(rng, n, k)
+    x = synth.gen_x(rng, m, k)
+    xd, wqd, wsd = dev_bf16(x), dev_u8(wq), dev_u8(ws)
+    outs = []
+    for _ in range(3):
+        outs.append(binding.nvfp4_gemm(xd, wqd, wsd, 1.0).cpu().numpy())
+    ws_t = binding.new_workspace(binding.gemm_workspace_bytes(m, n, k))
+    outs.append(binding.nvfp4_gemm(xd, wqd, wsd, 1.0, workspace=ws_t).cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+
+
+def test_workspace_reused_across_shapes():
+    """One caller workspace serves shapes with different tile counts in turn:
+    the split-K counters of one shape must never sit under another shape's
+    partial sums (regression: a 2-tile shape's partials used to overwrite
+    the counters of tiles 64..79 of a 5120-row shape)."""
+    rng = np.random.default_rng(9300)
+    shapes = [(68, 96, 2048), (17, 5120, 5120), (68, 96, 2048), (17, 5120, 5120), (33, 1000, 4096)]
+    need = max(binding.gemm_workspace_bytes(*s) for s in shapes)
+    ws_t = binding.new_workspace(need)
+    for m, n, k in shapes:
+        wq, ws = synth.gen_weights(rng, n, k)
+        x = synth.gen_x(rng, m, k)
+        print(f"[case] shared workspace M={m} N={n} K={k}", flush=True)
+        y = binding.nvfp4_gemm(dev_bf16(x), dev_u8(wq), dev_u8(ws), 1.0, workspace=ws_t).cpu().numpy()
+        y_ref, bound = oracle.nvfp4_gemm_ref(x, wq, ws, 1.0)
+        ok, worst, at = within_bound(y, y_ref, bound)
+        assert ok, f"M={m} N={n} K={k}: worst err/bound {worst:.3g} at {at}"

@@ -1,0 +1,172 @@
+"""GPU parity of the lm_head verify pass (argmax + greedy accept) against
+the CPU oracle (needs an MI355X).
+
+argmax must be exact on every decisive row (top-2 gap above the bound),
+accept_len exact on every decisive step; near ties are counted and
+reported, as the pages concede a batched verify may round the other way
+there (TandemLLM README, introduction)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev_bf16, dev_i32, dev_u8
+from verify_gemm_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_ex(x, wq, ws, g, drafts, T):
+    m = x.shape[0]
+    wsp = binding.new_workspace(binding.lmhead_workspace_bytes(m))
+    d = dev_i32(drafts.reshape(m // T, T - 1)) if T > 1 else None
+    am, al = binding.lmhead_argmax_accept_ex(dev_bf16(x), dev_u8(wq), dev_u8(ws), g, d, T, wsp)
+    torch.cuda.synchronize()
+    # the workspace is left zeroed for the next call
+    assert int(wsp.count_nonzero()) == 0
+    return am.cpu().numpy(), al.cpu().numpy()
+
+
+def make_drafts(rng, am, T, v):
+    """Drafts from the oracle argmax: mostly matching, with a mismatch at a
+    random position per sequence (or none)."""
+    s = am.size // T
+    a = am.reshape(s, T)
+    d = a[:, :T - 1].copy()
+    for q in range(s):
+        j = int(rng.integers(0, T))          # j == T-1: all match
+        if j < T - 1:
+            d[q, j] = (d[q, j] + 1 + int(rng.integers(0, v - 1))) % v if v > 1 else -1
+    return d.astype(np.int32)
+
+
+def check(x, wq, ws, g, T, rng, label):
+    m, k = x.shape
+    v = wq.shape[0]
+    print(f"[case] {label} M={m} T={T} K={k} V={v}", flush=True)
+    ref = oracle.lmhead_ref(x, wq, ws, g, T=T)
+    drafts = make_drafts(rng, ref["argmax"], T, v) if T > 1 else np.zeros((m, 0), np.int32)
+    ref = oracle.lmhead_ref(x, wq, ws, g, T=T, drafts=drafts)
+    am, al = run_ex(x, wq, ws, g, drafts, T)
+    dec = ref["decisive"]
+    assert np.array_equal(am[dec], ref["argmax"][dec]), f"{label}: argmax differs on a decisive row"
+    # near-tie rows must still pick one of the two contenders
+    nd = ~dec
+    assert np.all((am[nd] == ref["argmax"][nd]) | (am[nd] == ref["idx2"][nd]))
+    sd = ref["step_decisive"]
+    assert np.array_equal(al[:m // T][sd], ref["accept_len"][sd])
+    # accept_len is always consistent with the GPU's own argmax
+    for q in range(m // T):
+        assert al[q] == oracle.accept_len_ref(drafts.reshape(m // T, T - 1)[q], am[q * T:(q + 1) * T])
+    return int(nd.sum())
+
+
+@pytest.mark.parametrize("m,T", [(1, 1), (2, 2), (4, 1), (17, 17), (34, 17), (68, 17), (68, 68), (5, 5)])
+@pytest.mark.parametrize("k,v", [(5120, 1000), (1024, 4099), (48, 77), (272, 1)])
+def test_small_lmhead(m, T, k, v):
+    rng = np.random.default_rng(20000 + m * 101 + T * 7 + k + v)
+    wq, ws = synth.gen_weights(rng, v, k)
+    x = synth.gen_x(rng, m, k)
+    check(x, wq, ws, 0.875, T, rng, "small lm_head")
+
+
+@pytest.mark.parametrize("m", [1, 17, 68])
+def test_ties_pick_lowest_index(m):
+    rng = np.random.default_rng(21000 + m)
+    k, v = 1024, 3000
+    wq, ws = synth.gen_weights(rng, v, k)
+    x = synth.f32_to_bf16_bits(np.abs(rng.standard_normal((m, k))).astype(np.float32))
+    for r in (2047, 700, 2999):                   # identical dominant rows
+        wq[r] = 0x77
+        ws[r] = 0x48
+    ref = oracle.lmhead_ref(x, wq, ws, 1.0, T=1 if m == 1 else m)
+    assert np.all(ref["argmax"] == 700)
+    T = m
+    drafts = np.full((1, T - 1), 700, np.int32) if T > 1 else np.zeros((1, 0), np.int32)
+    am, al = run_ex(x, wq, ws, 1.0, drafts, T)
+    assert np.all(am == 700)
+    assert al[0] == T - 1
+
+
+def test_short_form_matches_ex():
+    rng = np.random.default_rng(22000)
+    k, v, m = 5120, 5000, 17
+    wq, ws = synth.gen_weights(rng, v, k)
+    x = synth.gen_x(rng, m, k)
+    ref = oracle.lmhead_ref(x, wq, ws, 1.0, T=m)
+    drafts = make_drafts(rng, ref["argmax"], m, v)
+    am1, al1 = binding.lmhead_argmax_accept(dev_bf16(x), dev_u8(wq), dev_u8(ws), dev_i32(drafts.reshape(-1)))
+    am2, al2 = run_ex(x, wq, ws, 1.0, drafts, m)
+    assert np.array_equal(am1.cpu().numpy(), am2)
+    assert int(al1.cpu()[0]) == int(al2[0])
+
+
+def test_graph_replay_matches_eager():
+    """Capture the lm_head pass once and replay it with new X: every replay
+    equals the eager result (the workspace resets itself, no memset)."""
+    rng = np.random.default_rng(23000)
+    k, v, m, T = 5120, 20000, 34, 17
+    wq, ws = synth.gen_weights(rng, v, k)
+    wqd, wsd = dev_u8(wq), dev_u8(ws)
+    xs = [synth.gen_x(rng, m, k) for _ in range(4)]
+    drafts = dev_i32(rng.integers(0, v, (m // T, T - 1)))
+    wsp = binding.new_workspace(binding.lmhead_workspace_bytes(m))
+    xbuf = dev_bf16(xs[0])
+    am = torch.empty(m, dtype=torch.int32, device="cuda")
+    al = torch.empty(m // T, dtype=torch.int32, device="cuda")
+    eager = []
+    for xb in xs:
+        xbuf.copy_(dev_bf16(xb))
+        binding.lmhead_argmax_accept_ex(xbuf, wqd, wsd, 1.0, drafts, T, wsp, am, al)
+        torch.cuda.synchronize()
+        eager.append((am.cpu().clone(), al.cpu().clone()))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            binding.lmhead_argmax_accept_ex(xbuf, wqd, wsd, 1.0, drafts, T, wsp, am, al)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, xb in enumerate(xs):
+            xbuf.copy_(dev_bf16(xb))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(am.cpu(), eager[i][0]), f"replay {rep} input {i}"
+            assert torch.equal(al.cpu(), eager[i][1])
+    assert int(wsp.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("v", [synth.VOCAB_SLICE, synth.VOCAB])
+def test_lmhead_1000_steps_golden(v):
+    """The 1000-step verify workload: M = 17, K = 5120, drafts equal the
+    oracle argmax with probability 0.7 (expected values from
+    tests/golden/make_lmhead_golden.py, which calls only the oracle)."""
+    path = os.path.join(GOLDEN, f"lmhead_v{v}_s1000.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    gold = np.load(path)
+    steps, T = int(gold["steps"]), int(gold["T"])
+    wq, ws, g = synth.lmhead_weights(v)
+    x = synth.lmhead_steps_x(steps, v)
+    print(f"[case] golden lm_head V={v} steps={steps}", flush=True)
+    xd, wqd, wsd = dev_bf16(x), dev_u8(wq), dev_u8(ws)
+    drafts = dev_i32(gold["drafts"])
+    wsp = binding.new_workspace(binding.lmhead_workspace_bytes(T))
+    am = torch.empty((steps, T), dtype=torch.int32, device="cuda")
+    al = torch.empty((steps,), dtype=torch.int32, device="cuda")
+    for s in range(steps):
+        binding.lmhead_argmax_accept_ex(xd[s * T:(s + 1) * T], wqd, wsd, g, drafts[s:s + 1], T, wsp,
+                                        am[s], al[s:s + 1])
+    torch.cuda.synchronize()
+    am, al = am.cpu().numpy(), al.cpu().numpy()
+    dec, sdec = gold["decisive"], gold["step_decisive"]
+    assert np.array_equal(am[dec], gold["argmax"][dec])
+    assert np.array_equal(al[sdec], gold["accept_len"][sdec])
+    print(f"V={v}: near-tie rows {int((~dec).sum())} of {dec.size}, near-tie steps "
+          f"{int((~sdec).sum())} of {steps}, argmax mismatches on near ties "
+          f"{int((am[~dec] != gold['argmax'][~dec]).sum())}, mean accept {al.mean():.3f}", flush=True)

@@ -1,0 +1,217 @@
+"""Thin ctypes binding of libvgemm.so: argument marshalling only.
+
+Every function checks that its torch tensors have the layout the C ABI
+expects (device, dtype, shape, contiguity), passes raw device pointers and
+the current HIP stream, and raises on a non-zero status.  All arithmetic
+happens in the HIP kernels; there is no fallback of any kind -- if the
+library is not built, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvgemm.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "vgemm.h")
+
+VG_OK = 0
+VG_MAX_M = 68
+VG_LMHEAD_K = 5120
+
+_lib = None
+
+
+class VgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libvgemm.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m verify_gemm_amd.build` "
+                          "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    sigs = {
+        "nvfp4_gemm": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp]),
+        "nvfp4_gemm_ex": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp, sz, vp]),
+        "vg_gemm_workspace_bytes": (sz, [i32, i32, i32]),
+        "lmhead_argmax_accept": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp]),
+        "lmhead_argmax_accept_ex": (i32, [vp, vp, vp, f32, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
+        "vg_lmhead_workspace_bytes": (sz, [i32]),
+        "vg_bwprobe": (i32, [vp, sz, vp, vp]),
+        "vg_bwprobe_sink_floats": (sz, []),
+        "vg_status_string": (ctypes.c_char_p, [i32]),
+        "vg_abi_version": (i32, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER) -> list[str]:
+    """Names of every function the public header declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return load().vg_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != VG_OK:
+        raise VgemmError(status, where)
+
+
+# --------------------------------------------------------------------------
+# torch marshalling
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _need(t, dtype, ndim: int, name: str):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _check_weights(wq, ws, k: int):
+    torch = _torch()
+    _need(wq, torch.uint8, 2, "Wq")
+    _need(ws, torch.uint8, 2, "Ws")
+    n = wq.shape[0]
+    if wq.shape[1] * 2 != k or tuple(ws.shape) != (n, k // 16):
+        raise ValueError(f"weights {tuple(wq.shape)}/{tuple(ws.shape)} do not match K={k}")
+    return n
+
+
+def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(load().vg_gemm_workspace_bytes(m, n, k))
+
+
+def lmhead_workspace_bytes(m: int) -> int:
+    return int(load().vg_lmhead_workspace_bytes(m))
+
+
+def new_workspace(nbytes: int, device=None):
+    """A zeroed device buffer for the _ex entry points (None if nbytes == 0)."""
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+def nvfp4_gemm(x, wq, ws, gscale: float, y=None, *, workspace=None, stream=None):
+    """Y[M][N] = gscale * X . dequant(Wq, Ws)^T (fp32).  x: bf16 [M][K];
+    wq: uint8 [N][K/2]; ws: uint8 [N][K/16].  With ``workspace`` (a zeroed
+    uint8 device tensor of gemm_workspace_bytes bytes) the _ex entry point
+    is used, otherwise the library-owned workspace."""
+    torch = _torch()
+    lib = load()
+    px = _need(x, torch.bfloat16, 2, "X")
+    m, k = x.shape
+    n = _check_weights(wq, ws, k)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    py = _need(y, torch.float32, 2, "Y")
+    if tuple(y.shape) != (m, n):
+        raise ValueError("Y must be [M][N]")
+    sp = _stream_ptr(stream)
+    if workspace is None:
+        st = lib.nvfp4_gemm(px, wq.data_ptr(), ws.data_ptr(), float(gscale), m, n, k, py, sp)
+    else:
+        pw = _need(workspace, torch.uint8, 1, "workspace")
+        st = lib.nvfp4_gemm_ex(px, wq.data_ptr(), ws.data_ptr(), float(gscale), m, n, k, py,
+                               pw, workspace.numel(), sp)
+    _check(st, "nvfp4_gemm")
+    return y
+
+
+def lmhead_argmax_accept(x, wq, ws, draft_ids=None, argmax=None, accept_len=None, *, stream=None):
+    """Short form: one sequence of T = M rows, K = 5120, tensor scale 1."""
+    torch = _torch()
+    lib = load()
+    px = _need(x, torch.bfloat16, 2, "X")
+    m, k = x.shape
+    if k != VG_LMHEAD_K:
+        raise ValueError(f"the short lm_head form needs K = {VG_LMHEAD_K}")
+    v = _check_weights(wq, ws, k)
+    pd = None
+    if draft_ids is not None:
+        pd = _need(draft_ids, torch.int32, 1, "draft_ids")
+        if draft_ids.numel() != m - 1:
+            raise ValueError("draft_ids must have M-1 entries")
+    argmax = argmax if argmax is not None else torch.empty(m, dtype=torch.int32, device=x.device)
+    accept_len = accept_len if accept_len is not None else torch.empty(1, dtype=torch.int32, device=x.device)
+    pa = _need(argmax, torch.int32, 1, "argmax")
+    pl = _need(accept_len, torch.int32, 1, "accept_len")
+    st = lib.lmhead_argmax_accept(px, wq.data_ptr(), ws.data_ptr(), pd, m, v, pa, pl, _stream_ptr(stream))
+    _check(st, "lmhead_argmax_accept")
+    return argmax, accept_len
+
+
+def lmhead_argmax_accept_ex(x, wq, ws, gscale: float, draft_ids, T: int, workspace,
+                            argmax=None, accept_len=None, *, stream=None):
+    """General form: S = M/T sequences; draft_ids int32 [S][T-1] (None iff T == 1);
+    workspace: zeroed uint8 device tensor of lmhead_workspace_bytes(M) bytes."""
+    torch = _torch()
+    lib = load()
+    px = _need(x, torch.bfloat16, 2, "X")
+    m, k = x.shape
+    v = _check_weights(wq, ws, k)
+    s = m // T if T > 0 else 0
+    pd = None
+    if draft_ids is not None:
+        pd = _need(draft_ids, torch.int32, 2, "draft_ids")
+        if tuple(draft_ids.shape) != (s, T - 1):
+            raise ValueError("draft_ids must be [M/T][T-1]")
+    argmax = argmax if argmax is not None else torch.empty(m, dtype=torch.int32, device=x.device)
+    accept_len = accept_len if accept_len is not None else torch.empty(max(s, 1), dtype=torch.int32, device=x.device)
+    pa = _need(argmax, torch.int32, 1, "argmax")
+    pl = _need(accept_len, torch.int32, 1, "accept_len")
+    pw = _need(workspace, torch.uint8, 1, "workspace")
+    st = lib.lmhead_argmax_accept_ex(px, wq.data_ptr(), ws.data_ptr(), float(gscale), pd, m, k, v, T,
+                                     pa, pl, pw, workspace.numel(), _stream_ptr(stream))
+    _check(st, "lmhead_argmax_accept_ex")
+    return argmax, accept_len
+
+
+def bwprobe(buf, sink, *, stream=None):
+    """Stream-read every byte of ``buf`` (a 16-byte-aligned device tensor)."""
+    lib = load()
+    nbytes = buf.numel() * buf.element_size()
+    st = lib.vg_bwprobe(buf.data_ptr(), nbytes, sink.data_ptr(), _stream_ptr(stream))
+    _check(st, "vg_bwprobe")
+
+
+def bwprobe_sink_floats() -> int:
+    return int(load().vg_bwprobe_sink_floats())

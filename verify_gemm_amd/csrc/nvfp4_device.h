@@ -1,0 +1,132 @@
+// Device-side building blocks for the NVFP4 weight pass on gfx950 (CDNA4).
+//
+// Element formats ("NVFP4 group-16", dgx-spark-qwen38 README, "The seven
+// targets"): E2M1 codes two per byte (element 2j = low nibble of byte j),
+// one E4M3 block scale per 16 K-elements, an fp32 tensor scale.
+//
+// Decoding uses the gfx950 conversion instructions:
+//   v_cvt_scalef32_pk_{f32,bf16}_fp4  two E2M1 codes of one byte -> two
+//     values, low nibble first.  Its scale operand contributes only its
+//     exponent, so it is always passed 1.0 here and the E4M3 scale (which
+//     has a mantissa) is applied with an ordinary multiply.
+//   v_cvt_scalef32_pk_f32_fp8  two E4M3 bytes -> two fp32, exact for every
+//     code including subnormals.
+// Every product x * s * e is exact in fp32 (8 + 4 + 2 significant bits) and
+// s * e is exact in bf16 (6 bits), so the only rounding is the fp32
+// accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vg {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---- loads -------------------------------------------------------------
+// Weight bytes are read exactly once per pass: nontemporal (streaming) hint.
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ unsigned short ld_stream(const unsigned short* p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ unsigned ld_stream(const unsigned* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ unsigned char ld_stream(const unsigned char* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// ---- decoding ----------------------------------------------------------
+// Two E4M3 scale bytes (low 16 bits of w) -> two fp32 values.
+__device__ __forceinline__ f32x2 e4m3x2_lo(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+}
+__device__ __forceinline__ f32x2 e4m3x2_hi(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+}
+
+// Byte `sel` of a code dword -> bf16 pair (element 2*sel, 2*sel+1), unscaled.
+template <int sel>
+__device__ __forceinline__ bf16x2 e2m1x2_bf16(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, sel);
+}
+// Byte `sel` of a code dword -> fp32 pair, unscaled.
+template <int sel>
+__device__ __forceinline__ f32x2 e2m1x2_f32(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, sel);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;  // exact: a = s * e has at most 6 significant bits
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// One code dword (8 elements of one 16-block) times its block scale s, as
+// the bf16x8 B-operand of an MFMA: element order is the K order.
+__device__ __forceinline__ bf16x8 dequant8_bf16(unsigned w, float s) {
+  f32x2 p0 = e2m1x2_f32<0>(w), p1 = e2m1x2_f32<1>(w), p2 = e2m1x2_f32<2>(w), p3 = e2m1x2_f32<3>(w);
+  u32x4 r;
+  r[0] = pack_bf16x2(p0[0] * s, p0[1] * s);
+  r[1] = pack_bf16x2(p1[0] * s, p1[1] * s);
+  r[2] = pack_bf16x2(p2[0] * s, p2[1] * s);
+  r[3] = pack_bf16x2(p3[0] * s, p3[1] * s);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// A dword holding two bf16 values as a bf16x2 operand.  The dword is taken
+// by value on purpose: __builtin_bit_cast applied directly to an element of
+// an ext_vector (x[1]) reinterprets the vector's first dword instead.
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned v) { return __builtin_bit_cast(bf16x2, v); }
+
+// sum_{j<8} x_j * e_j for one code dword against four dwords of bf16 pairs.
+__device__ __forceinline__ float dot8(unsigned w, u32x4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<0>(w), as_bf16x2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<1>(w), as_bf16x2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<2>(w), as_bf16x2(x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<3>(w), as_bf16x2(x.w), acc, false);
+  return acc;
+}
+
+// One 16-element block: codes (2 dwords), x (4 dwords-of-pairs x 2), scale.
+__device__ __forceinline__ float block16(unsigned c0, unsigned c1, u32x4 xa, u32x4 xb, float s,
+                                         float acc) {
+  float p = dot8(c0, xa, 0.0f);
+  p = dot8(c1, xb, p);
+  return __builtin_fmaf(s, p, acc);
+}
+
+// ---- reductions ----------------------------------------------------------
+template <int width>
+__device__ __forceinline__ float sum_lanes(float v) {
+#pragma unroll
+  for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ---- argmax keys -----------------------------------------------------------
+// A (logit, index) pair packed so that unsigned 64-bit max picks the larger
+// logit, and among equal logits the LOWER index.  -0 is canonicalised to +0
+// so that the two zeros compare equal, as they do as numbers.
+__device__ __forceinline__ unsigned long long argmax_key(float v, unsigned idx) {
+  v = v + 0.0f;  // -0 + 0 = +0 under round-to-nearest
+  unsigned u = __float_as_uint(v);
+  unsigned ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ unsigned key_index(unsigned long long key) {
+  return 0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull);
+}
+
+// Better = larger logit, then lower index.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+}  // namespace vg
