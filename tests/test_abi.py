@@ -77,24 +77,56 @@ def test_gemm_misaligned(lib, buf):
         assert lib.nvfp4_gemm(x, wq, ws, 1.0, 1, 16, 16, p, None) == VG_ERR_ALIGN
 
 
-def test_gemm_ex_workspace_checked(lib, buf):
+def test_gemm_ex_ignores_workspace(lib, buf):
     _, p = buf
-    need = lib.vg_gemm_workspace_bytes(17, 5120, 5120)
-    assert need > 0
-    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 5120, p, None, 0, None) == VG_ERR_WORKSPACE
-    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 5120, p, p, need - 1, None) == VG_ERR_WORKSPACE
+    assert lib.vg_gemm_workspace_bytes(17, 5120, 5120) == 0
+    # validation still applies to the _ex form
+    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 24, p, None, 0, None) == VG_ERR_SHAPE
 
 
 def test_workspace_sizes(lib):
-    assert lib.vg_gemm_workspace_bytes(1, 5120, 5120) == 0          # M = 1 never splits K
-    assert lib.vg_gemm_workspace_bytes(0, 5120, 5120) == 0
-    assert lib.vg_gemm_workspace_bytes(69, 5120, 5120) == 0
-    assert lib.vg_gemm_workspace_bytes(17, 5120, 23) == 0
-    small = lib.vg_gemm_workspace_bytes(17, 5120, 5120)
-    big = lib.vg_gemm_workspace_bytes(68, 5120, 5120)
-    assert 0 < small < big
-    assert lib.vg_lmhead_workspace_bytes(17) >= 8 * 68
+    for m, n, k in [(1, 5120, 5120), (17, 5120, 5120), (68, 5120, 17408), (0, 1, 16)]:
+        assert lib.vg_gemm_workspace_bytes(m, n, k) == 0
+    assert lib.vg_lmhead_workspace_bytes(17) >= 8 * 68 * 16
     assert lib.vg_lmhead_workspace_bytes(0) == 0 and lib.vg_lmhead_workspace_bytes(69) == 0
+
+
+def test_pass_create_validation(lib, buf):
+    """vg_pass_create rejects bad job lists before touching the device."""
+    _, p = buf
+    J = binding.GemmJob
+    L = binding.LmheadJob
+    out = ctypes.c_void_p()
+
+    def create(jobs, m, lm=None):
+        arr = (J * max(len(jobs), 1))(*jobs)
+        return lib.vg_pass_create(ctypes.cast(arr, ctypes.c_void_p), len(jobs), m,
+                                  ctypes.byref(lm) if lm is not None else None, ctypes.byref(out))
+
+    good = J(p, p, 1.0, 64, 128, p, p, 0)
+    assert lib.vg_pass_create(None, 1, 1, None, ctypes.byref(out)) == VG_ERR_NULL
+    assert lib.vg_pass_create(None, 0, 1, None, None) == VG_ERR_NULL
+    assert create([], 1) == VG_ERR_SHAPE                                   # nothing to run
+    assert create([good], 0) == VG_ERR_SHAPE
+    assert create([good], 69) == VG_ERR_UNSUPPORTED
+    assert create([J(p, p, 1.0, 64, 120, p, p, 0)], 1) == VG_ERR_SHAPE     # K % 16
+    assert create([J(p, None, 1.0, 64, 128, p, p, 0)], 1) == VG_ERR_NULL
+    assert create([J(p + 4, p, 1.0, 64, 128, p, p, 0)], 1) == VG_ERR_ALIGN
+    assert create([good, J(p, p, 1.0, 64, 128, p, p, -1)], 1) == VG_ERR_SHAPE   # negative stage
+    assert create([J(p, p, 1.0, 64, 128, p, p, 3), J(p, p, 1.0, 64, 128, p, p, 2)], 1) == VG_ERR_SHAPE
+    bad_lm = L(p, p, 1.0, 100, 5120, p, 5, p, p, p)                        # M % T != 0
+    assert create([good], 17, bad_lm) == VG_ERR_SHAPE
+    assert create([good], 17, L(p, p, 1.0, 100, 5120, p, 17, None, p, p)) == VG_ERR_NULL
+    assert out.value is None
+    lib.vg_pass_destroy(None)                                              # no-op
+
+
+def test_pass_handle_null_checks(lib):
+    e = ctypes.c_int()
+    assert lib.vg_pass_run(None, None) == VG_ERR_NULL
+    assert lib.vg_pass_run_unfused(None, None) == VG_ERR_NULL
+    assert lib.vg_pass_check(None, ctypes.byref(e)) == VG_ERR_NULL
+    assert lib.vg_pass_info(None, None, None, None) == VG_ERR_NULL
 
 
 def test_lmhead_validation(lib, buf):

@@ -1,0 +1,83 @@
+"""The full 64-layer step at its real size (449 NVFP4 matrices, 14.1 GB,
+generated on the device), in the launch configuration the benchmark times,
+checked against the oracle on sampled outputs and on the complete lm_head
+argmax / accept (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from verify_gemm_amd import synth, weightpass
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def weights():
+    w = weightpass.PassWeights("cuda")
+    torch.cuda.synchronize()
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+def host_bits(x):
+    return x.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("M", [1, 4, 17, 68])
+def test_full_step_sampled(weights, M):
+    print(f"[case] full step M={M}", flush=True)
+    run = weightpass.PassRun(weights, M)
+    run.run()
+    torch.cuda.synchronize()
+    assert run.check() == 0
+    rng = np.random.default_rng(40000 + M)
+    xs = {k: host_bits(v) for k, v in run.x.items()}
+    picks = [0, 3, 4, 6, 7 * 31 + 1, 7 * 31 + 5, 7 * 63 + 2, 7 * 63 + 6]
+    for idx in picks:
+        m = weights.mats[idx]
+        y = run.y[idx].cpu().numpy()
+        rows = rng.integers(0, m["n"], 24)
+        ms = rng.integers(0, M, 24)
+        wq = m["wq"][torch.from_numpy(rows).cuda()].cpu().numpy()
+        ws = m["ws"][torch.from_numpy(rows).cuda()].cpu().numpy()
+        pairs = list(zip(ms.tolist(), rows.tolist()))
+        ye, be = oracle.nvfp4_gemm_ref_entries(xs[m["k"]], wq, ws, m["g"], pairs)
+        got = np.array([y[a, b] for a, b in pairs], dtype=np.float64)
+        assert np.all(np.abs(got - ye) <= be), f"matrix {idx} ({m['name']}, layer {m['layer']})"
+    # the one-launch-per-matrix schedule gives the same bits on every output
+    first = [y.clone() for y in run.y] + [run.argmax.clone(), run.accept_len.clone()]
+    run.run_unfused()
+    torch.cuda.synchronize()
+    again = [y for y in run.y] + [run.argmax, run.accept_len]
+    for a, b in zip(first, again):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+    run.close()
+
+
+def test_full_step_lmhead_argmax_accept(weights):
+    """M = 17 (16 drafts + 1): the complete lm_head argmax over 248,320 rows
+    against the oracle; drafts follow the oracle's argmax with p = 0.7."""
+    M = 17
+    run = weightpass.PassRun(weights, M)
+    lm = weights.lmhead
+    x = host_bits(run.x[synth.HIDDEN])
+    wq, ws = lm["wq"].cpu().numpy(), lm["ws"].cpu().numpy()
+    ref = oracle.lmhead_ref(x, wq, ws, lm["g"], T=M)
+    drafts = synth.gen_drafts(np.random.default_rng(41000), ref["argmax"].reshape(1, M), synth.VOCAB)
+    run.set_drafts(torch.from_numpy(drafts).cuda())
+    ref = oracle.lmhead_ref(x, wq, ws, lm["g"], T=M, drafts=drafts)
+    run.run()
+    torch.cuda.synchronize()
+    assert run.check() == 0
+    am = run.argmax.cpu().numpy()
+    al = int(run.accept_len.cpu()[0])
+    dec = ref["decisive"]
+    assert np.array_equal(am[dec], ref["argmax"][dec])
+    if ref["step_decisive"][0]:
+        assert al == int(ref["accept_len"][0])
+    print(f"full-step lm_head: decisive rows {int(dec.sum())}/17, accept_len {al} "
+          f"(oracle {int(ref['accept_len'][0])})", flush=True)
+    run.close()

@@ -1,0 +1,174 @@
+"""GPU parity of the step executor (vg_pass_*): a whole step as one
+persistent launch, checked job by job against the CPU oracle, against the
+one-launch-per-matrix schedule (bitwise), across repeated launches and graph
+replays (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev_bf16, dev_i32, dev_u8, within_bound
+from verify_gemm_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def build(M, T, specs, lm_spec, seed):
+    """specs: list of (N, K, stage); lm_spec: (V, K) or None."""
+    rng = np.random.default_rng(seed)
+    host, gemms, ys = [], [], []
+    xs = {}
+    for n, k, stage in specs:
+        if k not in xs:
+            xs[k] = synth.gen_x(rng, M, k)
+        wq, ws = synth.gen_weights(rng, n, k)
+        g = synth.gen_gscale(rng)
+        y = torch.full((M, n), float("nan"), dtype=torch.float32, device="cuda")
+        host.append((xs[k], wq, ws, g))
+        ys.append(y)
+        gemms.append((None, dev_u8(wq), dev_u8(ws), g, y, stage))
+    xd = {k: dev_bf16(v) for k, v in xs.items()}
+    gemms = [(xd[specs[i][1]],) + gemms[i][1:] for i in range(len(gemms))]
+    lm = None
+    lmhost = None
+    if lm_spec is not None:
+        v, k = lm_spec
+        if k not in xs:
+            xs[k] = synth.gen_x(rng, M, k)
+            xd[k] = dev_bf16(xs[k])
+        wq, ws = synth.gen_weights(rng, v, k)
+        g = synth.gen_gscale(rng)
+        ref = oracle.lmhead_ref(xs[k], wq, ws, g, T=T)
+        drafts = ref["argmax"].reshape(M // T, T)[:, :T - 1].copy()
+        for q in range(M // T):                       # a mismatch at a random position
+            j = int(rng.integers(0, T))
+            if j < T - 1:
+                drafts[q, j] = (drafts[q, j] + 1) % v
+        am = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+        al = torch.full((M // T,), -7, dtype=torch.int32, device="cuda")
+        dd = dev_i32(drafts) if T > 1 else torch.zeros((M // T, 0), dtype=torch.int32, device="cuda")
+        lm = (xd[k], dev_u8(wq), dev_u8(ws), g, T, dd, am, al)
+        lmhost = (xs[k], wq, ws, g, drafts)
+    p = binding.Pass(gemms, M, lm)
+    return p, host, ys, lm, lmhost
+
+
+def check_outputs(M, T, host, ys, lm, lmhost, label):
+    for i, ((x, wq, ws, g), y) in enumerate(zip(host, ys)):
+        y_ref, bound = oracle.nvfp4_gemm_ref(x, wq, ws, g)
+        ok, worst, at = within_bound(y.cpu().numpy(), y_ref, bound)
+        assert ok, f"{label} job {i} N={wq.shape[0]} K={x.shape[1]}: worst err/bound {worst:.3g} at {at}"
+    if lm is not None:
+        x, wq, ws, g, drafts = lmhost
+        ref = oracle.lmhead_ref(x, wq, ws, g, T=T, drafts=drafts if T > 1 else None)
+        am = lm[6].cpu().numpy()
+        al = lm[7].cpu().numpy()
+        dec = ref["decisive"]
+        assert np.array_equal(am[dec], ref["argmax"][dec]), f"{label}: lm_head argmax"
+        if T > 1:
+            sd = ref["step_decisive"]
+            assert np.array_equal(al[sd], ref["accept_len"][sd]), f"{label}: accept_len"
+        else:
+            assert np.all(al == 0)
+
+
+def snapshot(ys, lm):
+    out = [y.clone() for y in ys]
+    if lm is not None:
+        out += [lm[6].clone(), lm[7].clone()]
+    return out
+
+
+def same(a, b):
+    return all(torch.equal(u.view(torch.int32) if u.dtype == torch.float32 else u,
+                           v.view(torch.int32) if v.dtype == torch.float32 else v) for u, v in zip(a, b))
+
+
+LAYER = [(5120, 5120, 0), (5120, 5120, 0), (5120, 5120, 0), (5120, 5120, 1),
+         (17408, 5120, 2), (17408, 5120, 2), (5120, 17408, 3)]
+
+
+@pytest.mark.parametrize("M,T", [(1, 1), (4, 1), (17, 17), (68, 17)])
+def test_one_layer_step(M, T):
+    print(f"[case] one-layer step M={M} T={T}", flush=True)
+    p, host, ys, lm, lmhost = build(M, T, LAYER, (20000, 5120), 31000 + M)
+    info = p.info()
+    assert info["jobs"] == 8 and info["stages"] == 5
+    p.run()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    check_outputs(M, T, host, ys, lm, lmhost, f"M={M}")
+    first = snapshot(ys, lm)
+    # repeated launches: the control block resets itself
+    for _ in range(3):
+        p.run()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    assert same(first, snapshot(ys, lm))
+    # the one-launch-per-matrix schedule computes the same bits
+    for y in ys:
+        y.fill_(float("nan"))
+    p.run_unfused()
+    torch.cuda.synchronize()
+    assert same(first, snapshot(ys, lm))
+    p.close()
+
+
+ODD = [(77, 48, 0), (300, 1040, 0), (1, 2048, 1), (129, 272, 2), (64, 1024, 2), (200, 5120, 3)]
+
+
+@pytest.mark.parametrize("M,T", [(1, 1), (2, 2), (17, 17), (34, 17), (68, 4)])
+def test_odd_shapes_step(M, T):
+    print(f"[case] odd-shape step M={M} T={T}", flush=True)
+    p, host, ys, lm, lmhost = build(M, T, ODD, (1000, 2048), 32000 + M)
+    p.run()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    check_outputs(M, T, host, ys, lm, lmhost, f"odd M={M}")
+    first = snapshot(ys, lm)
+    p.run_unfused()
+    torch.cuda.synchronize()
+    assert same(first, snapshot(ys, lm))
+    p.close()
+
+
+@pytest.mark.parametrize("M", [1, 17])
+def test_step_without_lmhead_and_lmhead_only(M):
+    p, host, ys, lm, lmhost = build(M, 1, LAYER[:4], None, 33000 + M)
+    p.run()
+    torch.cuda.synchronize()
+    check_outputs(M, 1, host, ys, None, None, "no lm_head")
+    p.close()
+    T = M
+    p, host, ys, lm, lmhost = build(M, T, [], (70000, 5120), 34000 + M)
+    p.run()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    check_outputs(M, T, host, ys, lm, lmhost, "lm_head only")
+    p.close()
+
+
+@pytest.mark.parametrize("M,T", [(1, 1), (17, 17)])
+def test_step_graph_replay(M, T):
+    """The single launch captured in a graph and replayed, with eager work
+    and synchronisation between replays: every replay equals the eager run."""
+    p, host, ys, lm, lmhost = build(M, T, LAYER[:4], (9000, 5120), 35000 + M)
+    p.run()
+    torch.cuda.synchronize()
+    eager = snapshot(ys, lm)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            p.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for y in ys:
+            y.fill_(0.0)
+        lm[6].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(eager, snapshot(ys, lm)), f"replay {rep}"
+    assert p.check() == 0
+    p.close()

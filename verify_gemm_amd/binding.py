@@ -37,6 +37,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m verify_gemm_amd.build` "
                           "(the HIP library is required, there is no fallback)")
+    # torch ships its own copy of the HIP runtime under the same soname
+    # (libamdhip64.so.7).  Importing torch first makes the dynamic loader
+    # bind this library to that copy, so the process has ONE runtime and
+    # torch's device pointers and streams are valid here; loading this
+    # library first would map /opt/rocm's copy as a second, separate runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
     sigs = {
@@ -46,6 +52,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lmhead_argmax_accept": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp]),
         "lmhead_argmax_accept_ex": (i32, [vp, vp, vp, f32, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
         "vg_lmhead_workspace_bytes": (sz, [i32]),
+        "vg_pass_create": (i32, [vp, i32, i32, vp, ctypes.POINTER(vp)]),
+        "vg_pass_run": (i32, [vp, vp]),
+        "vg_pass_run_unfused": (i32, [vp, vp]),
+        "vg_pass_check": (i32, [vp, ctypes.POINTER(i32)]),
+        "vg_pass_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+        "vg_pass_destroy": (None, [vp]),
         "vg_bwprobe": (i32, [vp, sz, vp, vp]),
         "vg_bwprobe_sink_floats": (sz, []),
         "vg_status_string": (ctypes.c_char_p, [i32]),
@@ -203,6 +215,93 @@ def lmhead_argmax_accept_ex(x, wq, ws, gscale: float, draft_ids, T: int, workspa
                                      pa, pl, pw, workspace.numel(), _stream_ptr(stream))
     _check(st, "lmhead_argmax_accept_ex")
     return argmax, accept_len
+
+
+class GemmJob(ctypes.Structure):
+    """vg_gemm_job of include/vgemm.h."""
+    _fields_ = [("Wq", ctypes.c_void_p), ("Ws", ctypes.c_void_p), ("gscale", ctypes.c_float),
+                ("N", ctypes.c_int), ("K", ctypes.c_int), ("X", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("stage", ctypes.c_int)]
+
+
+class LmheadJob(ctypes.Structure):
+    """vg_lmhead_job of include/vgemm.h."""
+    _fields_ = [("Wq", ctypes.c_void_p), ("Ws", ctypes.c_void_p), ("gscale", ctypes.c_float),
+                ("V", ctypes.c_int), ("K", ctypes.c_int), ("X", ctypes.c_void_p), ("T", ctypes.c_int),
+                ("draft_ids", ctypes.c_void_p), ("argmax", ctypes.c_void_p),
+                ("accept_len", ctypes.c_void_p)]
+
+
+class Pass:
+    """A whole step (vg_pass_*): GEMM jobs in dependency order plus an
+    optional lm_head job, run as one persistent launch.  ``gemms`` is a list
+    of (x, wq, ws, gscale, y, stage) with torch device tensors; ``lmhead`` is
+    (x, wq, ws, gscale, T, drafts, argmax, accept_len) or None.  The tensors
+    must outlive the Pass (it keeps references)."""
+
+    def __init__(self, gemms, M: int, lmhead=None):
+        torch = _torch()
+        lib = load()
+        self._keep = []
+        arr = (GemmJob * max(len(gemms), 1))()
+        for i, (x, wq, ws, g, y, stage) in enumerate(gemms):
+            _need(x, torch.bfloat16, 2, "X")
+            _need(y, torch.float32, 2, "Y")
+            k = x.shape[1]
+            n = _check_weights(wq, ws, k)
+            if tuple(y.shape) != (M, n) or x.shape[0] != M:
+                raise ValueError("X must be [M][K] and Y [M][N]")
+            arr[i] = GemmJob(wq.data_ptr(), ws.data_ptr(), float(g), n, k, x.data_ptr(), y.data_ptr(),
+                             int(stage))
+            self._keep += [x, wq, ws, y]
+        lm = None
+        if lmhead is not None:
+            x, wq, ws, g, T, drafts, am, al = lmhead
+            _need(x, torch.bfloat16, 2, "X")
+            k = x.shape[1]
+            v = _check_weights(wq, ws, k)
+            _need(am, torch.int32, 1, "argmax")
+            _need(al, torch.int32, 1, "accept_len")
+            pd = None
+            if T > 1:
+                pd = _need(drafts, torch.int32, 2, "draft_ids")
+            lm = LmheadJob(wq.data_ptr(), ws.data_ptr(), float(g), v, k, x.data_ptr(), int(T), pd,
+                           am.data_ptr(), al.data_ptr())
+            self._keep += [x, wq, ws, drafts, am, al]
+        h = ctypes.c_void_p()
+        st = lib.vg_pass_create(ctypes.cast(arr, ctypes.c_void_p), len(gemms), int(M),
+                                ctypes.byref(lm) if lm is not None else None, ctypes.byref(h))
+        _check(st, "vg_pass_create")
+        self._lib = lib
+        self.handle = h
+
+    def run(self, stream=None):
+        _check(self._lib.vg_pass_run(self.handle, _stream_ptr(stream)), "vg_pass_run")
+
+    def run_unfused(self, stream=None):
+        _check(self._lib.vg_pass_run_unfused(self.handle, _stream_ptr(stream)), "vg_pass_run_unfused")
+
+    def check(self) -> int:
+        e = ctypes.c_int(0)
+        _check(self._lib.vg_pass_check(self.handle, ctypes.byref(e)), "vg_pass_check")
+        return int(e.value)
+
+    def info(self):
+        a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check(self._lib.vg_pass_info(self.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+               "vg_pass_info")
+        return {"jobs": a.value, "stages": b.value, "items": c.value}
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self._lib.vg_pass_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def bwprobe(buf, sink, *, stream=None):

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvgemm.so")
-SOURCES = ["api.cpp", "gemv_m1.hip", "gemm_mfma.hip", "bwprobe.hip"]
+SOURCES = ["api.cpp", "stream.hip", "bwprobe.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code: hipcc may form

@@ -1,6 +1,6 @@
-// Internal launcher interface between the C-ABI layer (api.cpp) and the
-// kernels.  Every launcher assumes its arguments were validated by the
-// caller and returns the hipError_t of the launch.
+// Internal interface between the C-ABI layer (api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the caller and
+// returns the hipError_t of the launch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,38 +9,67 @@
 
 namespace vg {
 
-// Split-K bookkeeping of the MFMA GEMM: how many K-splits a shape uses and
-// how the caller's workspace is carved up.
-struct GemmPlan {
-  int mt;          // 16-row M-tiles (1..5)
-  int nt;          // 16-row N-tiles per wave
-  int ntiles;      // N-tiles of 16*nt rows
-  int splits;      // K-splits (1 = no workspace)
-  int kchunk;      // K elements per split (multiple of 128 unless splits == 1)
-  size_t counter_bytes;
-  size_t partial_bytes;
-  size_t workspace_bytes() const { return splits > 1 ? counter_bytes + partial_bytes : 0; }
-};
-GemmPlan plan_gemm(int M, int N, int K);
+constexpr int VG_MAX_M_DEV = 68;
+constexpr int kKeySlots = 16;     // atomic-max slots per lm_head row
+constexpr int kMaxStages = 1024;  // dependency stages of one step
 
-// Workspace of the lm_head pass: arg-max keys + an arrival counter.
-struct LmheadWorkspace {
-  unsigned long long keys[128];
-  unsigned counter;
-  unsigned pad[63];
+// One NVFP4 matrix of a step.  Items are contiguous blocks of
+// rows_per_item weight rows (all of K); jobs are listed in pass order and
+// their items are numbered consecutively from item_begin.
+struct StreamJob {
+  const uint8_t* wq;  // [n][k/2]
+  const uint8_t* ws;  // [n][k/16]
+  const uint16_t* x;  // [M][k] bf16 bits
+  float* y;           // [M][n] (kind 0)
+  float g;
+  int n;
+  int k;
+  int stage;          // dependency stage (non-decreasing along the list)
+  int item_begin;
+  int items;
+  int kind;           // 0: GEMM, 1: lm_head (argmax, no output matrix)
+  int pad;
 };
 
-hipError_t launch_gemv_m1(const uint16_t* X, const uint8_t* Wq, const uint8_t* Ws, float g, int N,
-                          int K, float* Y, hipStream_t stream);
-hipError_t launch_gemm_mfma(const uint16_t* X, const uint8_t* Wq, const uint8_t* Ws, float g, int M,
-                            int N, int K, float* Y, void* workspace, const GemmPlan& plan,
-                            hipStream_t stream);
-hipError_t launch_lmhead_m1(const uint16_t* X, const uint8_t* Wq, const uint8_t* Ws, float g, int K,
-                            int V, const int32_t* drafts, int32_t* argmax, int32_t* accept_len,
-                            LmheadWorkspace* ws, hipStream_t stream);
-hipError_t launch_lmhead_mfma(const uint16_t* X, const uint8_t* Wq, const uint8_t* Ws, float g,
-                              int M, int K, int V, int T, const int32_t* drafts, int32_t* argmax,
-                              int32_t* accept_len, LmheadWorkspace* ws, hipStream_t stream);
+// Device-side control block of a streaming launch.  It must be zero before
+// the first launch; every launch leaves it zero again (the last workgroup
+// out resets it), except `error`, which stays set once a stage wait timed
+// out so the host can see it.
+struct StreamCtl {
+  unsigned ticket;
+  unsigned exits;
+  unsigned error;
+  unsigned pad;
+  unsigned long long keys[VG_MAX_M_DEV][kKeySlots];
+  unsigned stage_done[kMaxStages];
+};
+
+struct StreamArgs {
+  StreamJob job0;                // the job of a single-job launch
+  const StreamJob* jobs;         // device array (ticket mode)
+  const unsigned* stage_total;   // device array: items per stage (ticket mode)
+  StreamCtl* ctl;                // device control block (grid/ticket modes)
+  int njobs;
+  int nstages;
+  int total_items;
+  int M;                         // rows of every X
+  int T;                         // lm_head rows per sequence
+  int has_lmhead;
+  const int32_t* drafts;         // [M/T][T-1]
+  int32_t* argmax;               // [M]
+  int32_t* accept_len;           // [M/T]
+};
+
+enum StreamMode { STREAM_DIRECT = 0, STREAM_GRID = 1, STREAM_TICKET = 2 };
+
+// 0 for the M = 1 path, else the number of 16-row M-tiles.
+int stream_mt_class(int M);
+// Weight rows per item for a batch of M rows and a reduction length K.
+int stream_rows_per_item(int M, int K);
+// DIRECT: grid = items of a.job0.  GRID: a.job0 walked by up to `grid`
+// resident workgroups.  TICKET: the job list, up to `grid` workgroups.
+hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream);
+
 hipError_t launch_bwprobe(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 size_t bwprobe_sink_floats();
 

@@ -1,0 +1,729 @@
+// The NVFP4 weight-streaming kernels: one code path for a single GEMM, the
+// lm_head verify pass, and the whole decode / verify step.
+//
+// A step of the ~27B hybrid reads every weight once and is bound by memory
+// bandwidth (ling-engine README, opening paragraph and "Six levers";
+// veloGB10 docs, "Engineered to the roofline").  Measured on MI355X, a
+// workgroup that streams one contiguous region sustains a higher read rate
+// than a grid-stride walk, and every kernel launch costs a few microseconds
+// of ramp-up and drain -- as long as streaming a whole 5120x5120 NVFP4
+// matrix.  So the unit of work here is an ITEM: a contiguous block of
+// weight rows (all of K) handled by one 256-thread workgroup, and a step is
+// one persistent launch that streams items back to back:
+//
+//   * items are handed out in pass order by an atomic ticket.  An item of
+//     stage s (the per-layer order {q,k,v} -> o -> {gate,up} -> down ->
+//     ... -> lm_head) may only consume its activations once every item of
+//     stage s-1 has finished; a workgroup issues the item's weight loads
+//     FIRST (weights never depend on activations) and only then waits on
+//     the stage counter, so HBM keeps streaming across the dependency.
+//     Tickets are taken in order, so every item a waiter depends on is
+//     already held by a running workgroup: no co-residency is assumed and
+//     the wait cannot deadlock (it is bounded anyway and raises an error
+//     flag instead of hanging);
+//   * M = 1 (plain decode): each half-wave owns a weight row, lane L reads
+//     16-byte chunks L, L+32, ... (512 contiguous bytes per half-wave and
+//     instruction, nontemporal); per 16-block eight v_dot2_f32_bf16 multiply
+//     the unscaled E2M1 values (exact in bf16) with X and one FMA applies
+//     the E4M3 block scale (~1.1 VALU ops per weight element);
+//   * M >= 2 (verify, 17 or 68 rows): v_mfma_f32_16x16x32_bf16 on weights
+//     dequantised exactly to bf16 (E4M3 x E2M1 has <= 6 significant bits);
+//     an item is 16*NT weight rows, the four waves take a quarter of K
+//     each, stream their windows through a register ring of P 128-element
+//     windows, and meet in LDS where the four partial tiles are added in a
+//     fixed order -- no global partial sums and no float atomics, so every
+//     result is bitwise repeatable;
+//   * the lm_head never writes logits: each workgroup keeps the best
+//     (logit, lowest index) per row across its items and publishes it once
+//     as a 64-bit key with an unsigned atomic max into one of 16 slots per
+//     row (spreading the atomics); the last workgroup to leave reads the
+//     slots, writes argmax, runs the greedy accept rule per sequence
+//     (TandemLLM README, introduction: keep the longest agreeing prefix, the
+//     target's own token replaces the first wrong guess) and zeroes the
+//     control block for the next launch -- no host memset, so a step can be
+//     replayed from a graph.
+#include "launch.h"
+#include "nvfp4_device.h"
+
+namespace vg {
+
+namespace {
+
+constexpr int kWG = 256;
+constexpr int kWaves = kWG / kWave;
+constexpr long kSpinLimit = 1L << 23;  // ~0.2 s of polling before giving up
+
+// ---------------------------------------------------------------------------
+// control block helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Output stores are agent-coherent (they write through the XCD's L2), so
+// a consumer on another XCD sees them once the producer's count is visible.
+__device__ __forceinline__ void store_out(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 polls until stage `s` has `target` finished items.
+__device__ bool wait_stage(StreamCtl* ctl, int s, unsigned target) {
+  for (long it = 0; it < kSpinLimit; ++it) {
+    if (ld_agent(&ctl->stage_done[s]) >= target) {
+      // agent-scope acquire: drop stale lines so this workgroup's later
+      // activation reads see what the previous stage wrote
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  st_agent(&ctl->error, 1u);
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// M = 1 items
+// ---------------------------------------------------------------------------
+// CPL = K / 1024 chunks per lane (compile time), RH rows per half-wave: a
+// wave owns 2*RH rows, an item 8*RH rows.  All weight loads of the item are
+// issued by issue(); compute() needs the activations.
+template <int CPL, int RH>
+struct GemvItem {
+  static constexpr int kRows = 2 * RH * kWaves;
+  u32x4 q[CPL][RH];
+  unsigned short sc[CPL][RH];
+  int row0;
+
+  __device__ __forceinline__ void issue(const StreamJob& j, int item) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, L = lane & 31;
+    row0 = item * kRows + w * 2 * RH;
+    const size_t rb = (size_t)j.k >> 1, sb = (size_t)j.k >> 4;
+#pragma unroll
+    for (int i = 0; i < RH; ++i) {
+      int r = row0 + 2 * i + h;
+      r = r < j.n ? r : j.n - 1;  // rows past N re-read the last row; never stored
+      const u32x4* wp = reinterpret_cast<const u32x4*>(j.wq + (size_t)r * rb);
+      const unsigned short* sp = reinterpret_cast<const unsigned short*>(j.ws + (size_t)r * sb);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        q[c][i] = ld_stream(wp + L + 32 * c);
+        sc[c][i] = ld_stream(sp + L + 32 * c);
+      }
+    }
+  }
+
+  // Row sums (identical in every lane of the half-wave) times g.
+  __device__ __forceinline__ void compute(const StreamJob& j, float (&acc)[RH]) {
+    const int L = threadIdx.x & 31;
+    const u32x4* xp = reinterpret_cast<const u32x4*>(j.x);
+#pragma unroll
+    for (int i = 0; i < RH; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = L + 32 * c;
+      const u32x4 x0 = xp[4 * ch], x1 = xp[4 * ch + 1], x2 = xp[4 * ch + 2], x3 = xp[4 * ch + 3];
+#pragma unroll
+      for (int i = 0; i < RH; ++i) {
+        const f32x2 s = e4m3x2_lo(sc[c][i]);
+        acc[i] = block16(q[c][i][0], q[c][i][1], x0, x1, s[0], acc[i]);
+        acc[i] = block16(q[c][i][2], q[c][i][3], x2, x3, s[1], acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RH; ++i) acc[i] = sum_lanes<32>(acc[i]) * j.g;
+  }
+
+  __device__ __forceinline__ int row(int i) const { return row0 + 2 * i + ((threadIdx.x & 63) >> 5); }
+};
+
+// Any K % 16 == 0: each wave owns one row of a 4-row item and walks it in
+// 16-element blocks (8 code bytes, one scale byte).  Loads are issued in
+// compute(); this path serves shapes outside the tuned ones.
+struct GemvGenericItem {
+  static constexpr int kRows = kWaves;
+  int r;
+  __device__ __forceinline__ void issue(const StreamJob& j, int item) {
+    r = item * kRows + (threadIdx.x >> 6);
+  }
+  __device__ __forceinline__ float compute(const StreamJob& j) {
+    const int lane = threadIdx.x & 63;
+    const int rr = r < j.n ? r : j.n - 1;
+    const int nb = j.k >> 4;
+    const uint8_t* wrow = j.wq + (size_t)rr * (j.k >> 1);
+    const uint8_t* srow = j.ws + (size_t)rr * nb;
+    float acc = 0.0f;
+    for (int b = lane; b < nb; b += kWave) {
+      const unsigned* cw = reinterpret_cast<const unsigned*>(wrow + 8 * (size_t)b);
+      const unsigned c0 = ld_stream(cw), c1 = ld_stream(cw + 1);
+      const float s = e4m3x2_lo(ld_stream(srow + b))[0];
+      const u32x4* xb = reinterpret_cast<const u32x4*>(j.x + 16 * (size_t)b);
+      acc = block16(c0, c1, xb[0], xb[1], s, acc);
+    }
+    return sum_lanes<64>(acc) * j.g;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// M >= 2 items (MFMA)
+// ---------------------------------------------------------------------------
+// Lane (c = lane % 16, gq = lane / 16) streams, per 128-element window, the
+// 16-byte code chunk [kwin/2 + 16gq, +16) of row n0 + 16*nt + c and the two
+// scale bytes of its 32 elements.  Code dword t is the B operand of MFMA
+// step t (K positions kwin + 32gq + 8t + j); X is read in the same order (a
+// consistent permutation of K leaves the dot product unchanged).
+template <int MT, int NT, int P, bool XPF>
+struct MfmaItem {
+  static_assert(P % 2 == 0, "ring depth must be even");
+  static constexpr int kRows = 16 * NT;
+  u32x4 q[P][NT];
+  unsigned short sc[P][NT];
+  f32x4 acc[MT][NT];
+  const uint8_t* wrow[NT];
+  const uint8_t* srow[NT];
+  int n0, w0, nwin;
+
+  __device__ __forceinline__ void load_window(int slot_win, u32x4 (&qq)[NT], unsigned short (&ss)[NT]) {
+    const int gq = (threadIdx.x & 63) >> 4;
+    const int kwin = slot_win * 128;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      qq[nt] = ld_stream(reinterpret_cast<const u32x4*>(wrow[nt] + (kwin >> 1)) + gq);
+      ss[nt] = ld_stream(reinterpret_cast<const unsigned short*>(srow[nt] + (kwin >> 4)) + gq);
+    }
+  }
+
+  // K must be a multiple of 128 here (whole windows); the wave's quarter of
+  // the windows is [w0, w0 + nwin).
+  __device__ __forceinline__ void issue(const StreamJob& j, int item) {
+    const int lane = threadIdx.x & 63, c = lane & 15, w = threadIdx.x >> 6;
+    n0 = item * kRows;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      int n = n0 + 16 * nt + c;
+      n = n < j.n ? n : j.n - 1;
+      wrow[nt] = j.wq + (size_t)n * (size_t)(j.k >> 1);
+      srow[nt] = j.ws + (size_t)n * (size_t)(j.k >> 4);
+    }
+    const int nw = j.k >> 7;
+    w0 = (w * nw) / kWaves;
+    nwin = ((w + 1) * nw) / kWaves - w0;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (p < nwin) load_window(w0 + p, q[p], sc[p]);
+  }
+
+  __device__ __forceinline__ void load_x(const StreamJob& j, int M, int win, u32x4 (&xa)[MT][4]) {
+    const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+    const int e0 = win * 128 + 32 * gq;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + c;
+      const u32x4* xr = reinterpret_cast<const u32x4*>(j.x + (size_t)(m < M ? m : 0) * j.k + e0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) xa[mt][st] = m < M ? xr[st] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  __device__ __forceinline__ void mma_window(const u32x4 (&qq)[NT], const unsigned short (&ss)[NT],
+                                             const u32x4 (&xa)[MT][4]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 b[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const f32x2 s = e4m3x2_lo(ss[nt]);
+        b[nt] = dequant8_bf16(qq[nt][st], st < 2 ? s[0] : s[1]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[mt][st]), b[nt],
+                                                                acc[mt][nt], 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void compute(const StreamJob& j, int M) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (XPF) {
+      // activations double-buffered: window wi uses buffer wi & 1 (P even,
+      // so the parity of wi is the parity of the ring slot p)
+      u32x4 xa[2][MT][4];
+      if (nwin > 0) load_x(j, M, w0, xa[0]);
+      for (int base = 0; base < nwin; base += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int wi = base + p;
+          if (wi < nwin) {
+            if (wi + 1 < nwin) load_x(j, M, w0 + wi + 1, xa[(p + 1) & 1]);
+            mma_window(q[p], sc[p], xa[p & 1]);
+            if (wi + P < nwin) load_window(w0 + wi + P, q[p], sc[p]);
+          }
+        }
+      }
+    } else {
+      u32x4 xa[MT][4];
+      for (int base = 0; base < nwin; base += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int wi = base + p;
+          if (wi < nwin) {
+            load_x(j, M, w0 + wi, xa);
+            mma_window(q[p], sc[p], xa);
+            if (wi + P < nwin) load_window(w0 + wi + P, q[p], sc[p]);
+          }
+        }
+      }
+    }
+  }
+};
+
+// Any K % 16 == 0, predicated everywhere: each wave takes a quarter of the
+// (possibly partial) 128-element windows.
+template <int MT, int NT>
+struct MfmaGuardedItem {
+  static constexpr int kRows = 16 * NT;
+  f32x4 acc[MT][NT];
+  int n0;
+  __device__ __forceinline__ void issue(const StreamJob&, int item) { n0 = item * kRows; }
+  __device__ __forceinline__ void compute(const StreamJob& j, int M) {
+    const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4, w = threadIdx.x >> 6;
+    const uint8_t* wrow[NT];
+    const uint8_t* srow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      int n = n0 + 16 * nt + c;
+      n = n < j.n ? n : j.n - 1;
+      wrow[nt] = j.wq + (size_t)n * (size_t)(j.k >> 1);
+      srow[nt] = j.ws + (size_t)n * (size_t)(j.k >> 4);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nw = (j.k + 127) >> 7;
+    const int wb = (w * nw) / kWaves, we = ((w + 1) * nw) / kWaves;
+    for (int win = wb; win < we; ++win) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int e0 = win * 128 + 32 * gq + 8 * st;
+        const bool ok = e0 < j.k;  // K % 16 == 0: an 8-element piece is all in or all out
+        bf16x8 b[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          unsigned wd = 0;
+          float s = 0.0f;
+          if (ok) {
+            wd = ld_stream(reinterpret_cast<const unsigned*>(wrow[nt] + (e0 >> 1)));
+            s = e4m3x2_lo(ld_stream(srow[nt] + (e0 >> 4)))[0];
+          }
+          b[nt] = dequant8_bf16(wd, s);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = 16 * mt + c;
+          u32x4 a = {0u, 0u, 0u, 0u};
+          if (ok && m < M) a = *reinterpret_cast<const u32x4*>(j.x + (size_t)m * j.k + e0);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b[nt],
+                                                                  acc[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+// The four waves' partial tiles meet in LDS and are added in wave order
+// 0+1+2+3 by wave 0, which then owns the finished tile (times g).
+template <int MT, int NT>
+__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[MT][NT], float* red, float g) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int kVals = MT * NT * 4;
+  __syncthreads();  // red may still be read by the previous item's wave 0
+  if (w > 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          red[((w - 1) * kVals + (mt * NT + nt) * 4 + r) * kWave + lane] = acc[mt][nt][r];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[mt][nt][r];
+#pragma unroll
+          for (int ow = 0; ow < kWaves - 1; ++ow) v += red[(ow * kVals + (mt * NT + nt) * 4 + r) * kWave + lane];
+          acc[mt][nt][r] = v * g;
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-workgroup running best for the lm_head
+// ---------------------------------------------------------------------------
+template <int R>
+struct Best {
+  float v[R];
+  int i[R];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int r = 0; r < R; ++r) { v[r] = -__builtin_inff(); i[r] = -1; }
+  }
+  __device__ __forceinline__ void offer(int r, float val, int idx) {
+    if (i[r] < 0 || better(val, idx, v[r], i[r])) { v[r] = val; i[r] = idx; }
+  }
+};
+
+__device__ __forceinline__ void publish_best(StreamCtl* ctl, int m, float v, int idx) {
+  if (idx < 0) return;
+  const int slot = blockIdx.x % kKeySlots;
+  __hip_atomic_fetch_max(&ctl->keys[m][slot], argmax_key(v, (unsigned)idx), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+// MODE_DIRECT: grid = items of one job, no control block (GEMM calls).
+// MODE_GRID:   one job, each workgroup walks items blockIdx.x + i*gridDim.x
+//              (the standalone lm_head pass).
+// MODE_TICKET: the job list of a whole step, items by atomic ticket with
+//              stage waits (the persistent step kernel).
+constexpr int MODE_DIRECT = STREAM_DIRECT, MODE_GRID = STREAM_GRID, MODE_TICKET = STREAM_TICKET;
+
+template <int MT>
+struct Cfg;  // MT = 0: the M = 1 GEMV path
+template <>
+struct Cfg<0> {
+  static constexpr int NT = 0;
+};
+template <int MT>
+struct Cfg {
+  static constexpr int NT = MT <= 2 ? 2 : 4;   // weight rows per item: 32 or 64
+  static constexpr int P = MT <= 2 ? 6 : 2;    // 128-element windows in flight per wave (even)
+  static constexpr bool XPF = MT <= 2;         // prefetch the next window's activations
+};
+
+// Processes one item of job j.  `dep` is called by every thread after the
+// weight loads are in flight and before any activation is read; it returns
+// false if the stage wait failed (then nothing is stored).
+template <int CPL, int RH, class Dep, class BestT>
+__device__ __forceinline__ void gemv_run(const StreamJob& j, int item, Dep&& dep, BestT& best) {
+  GemvItem<CPL, RH> it;
+  it.issue(j, item);
+  const bool ok = dep();
+  float acc[RH];
+  it.compute(j, acc);
+  if (!ok) return;
+  if (j.kind == 0) {
+    if ((threadIdx.x & 31) == 0) {
+#pragma unroll
+      for (int i = 0; i < RH; ++i) {
+        const int r = it.row(i);
+        if (r < j.n) store_out(&j.y[r], acc[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RH; ++i) {
+      const int r = it.row(i);
+      if (r < j.n) best.offer(0, acc[i], r);
+    }
+  }
+}
+
+template <class Dep, class BestT>
+__device__ __forceinline__ void gemv_generic_run(const StreamJob& j, int item, Dep&& dep, BestT& best) {
+  GemvGenericItem it;
+  it.issue(j, item);
+  const bool ok = dep();
+  const float v = it.compute(j);
+  if (!ok || it.r >= j.n) return;
+  if (j.kind == 0) {
+    if ((threadIdx.x & 63) == 0) store_out(&j.y[it.r], v);
+  } else {
+    best.offer(0, v, it.r);
+  }
+}
+
+template <int MT, int NT, class Item, class Dep, class BestT>
+__device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item, int M, Dep&& dep,
+                                         float* red, BestT& best) {
+  it.issue(j, item);
+  const bool ok = dep();
+  it.compute(j, M);
+  reduce_waves<MT, NT>(it.acc, red, j.g);
+  if (!ok || (threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * mt + 4 * gq + r;
+      if (m < M) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = it.n0 + 16 * nt + c;
+          if (n < j.n) {
+            if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], it.acc[mt][nt][r]);
+            else best.offer(mt * 4 + r, it.acc[mt][nt][r], n);
+          }
+        }
+      }
+    }
+}
+
+template <int MT, class Dep, class BestT>
+__device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, Dep&& dep, float* red,
+                                         BestT& best) {
+  if constexpr (MT == 0) {
+    if (j.k == 5120) gemv_run<5, 4>(j, item, dep, best);
+    else if (j.k == 17408) gemv_run<17, 1>(j, item, dep, best);
+    else if (j.k == 1024) gemv_run<1, 8>(j, item, dep, best);
+    else gemv_generic_run(j, item, dep, best);
+  } else {
+    constexpr int NT = Cfg<MT>::NT;
+    if ((j.k & 127) == 0) {
+      MfmaItem<MT, NT, Cfg<MT>::P, Cfg<MT>::XPF> it;
+      mfma_run<MT, NT>(it, j, item, M, dep, red, best);
+    } else {
+      MfmaGuardedItem<MT, NT> it;
+      mfma_run<MT, NT>(it, j, item, M, dep, red, best);
+    }
+  }
+}
+
+// Publish the workgroup's lm_head bests (M = 1: every wave's best; M >= 2:
+// wave 0's per-lane bests reduced over the 16 lanes sharing rows).
+template <int MT, class BestT>
+__device__ __forceinline__ void publish(StreamCtl* ctl, int M, BestT& best) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if constexpr (MT == 0) {
+    float v = best.v[0];
+    int i = best.i[0];
+    const float ov = __shfl_xor(v, 32, kWave);
+    const int oi = __shfl_xor(i, 32, kWave);
+    if (oi >= 0 && (i < 0 || better(ov, oi, v, i))) { v = ov; i = oi; }
+    if (lane == 0) publish_best(ctl, 0, v, i);
+  } else {
+    if (w != 0) return;
+    const int c = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = best.v[mt * 4 + r];
+        int i = best.i[mt * 4 + r];
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+          const float ov = __shfl_xor(v, off, kWave);
+          const int oi = __shfl_xor(i, off, kWave);
+          if (oi >= 0 && (i < 0 || better(ov, oi, v, i))) { v = ov; i = oi; }
+        }
+        const int m = 16 * mt + 4 * gq + r;
+        if (c == 0 && m < M) publish_best(ctl, m, v, i);
+      }
+  }
+}
+
+// The last workgroup out: argmax from the key slots, greedy accept, reset.
+__device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am) {
+  const int tid = threadIdx.x;
+  if (a.has_lmhead) {
+    for (int m = tid; m < a.M; m += kWG) {
+      unsigned long long best = 0;
+      for (int s = 0; s < kKeySlots; ++s) {
+        const unsigned long long k =
+            __hip_atomic_load(&ctl->keys[m][s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        best = k > best ? k : best;
+        __hip_atomic_store(&ctl->keys[m][s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const int am = (int)key_index(best);
+      lds_am[m] = am;
+      a.argmax[m] = am;
+    }
+    __syncthreads();
+    const int S = a.M / a.T;
+    for (int q = tid; q < S; q += kWG) {
+      int L = 0;
+      const int32_t* d = a.drafts + (size_t)q * (a.T - 1);
+      while (L < a.T - 1 && d[L] == lds_am[q * a.T + L]) ++L;
+      a.accept_len[q] = L;
+    }
+  }
+  for (int s = tid; s < a.nstages; s += kWG) st_agent(&ctl->stage_done[s], 0u);
+  if (tid == 0) {
+    st_agent(&ctl->ticket, 0u);
+    st_agent(&ctl->exits, 0u);
+  }
+}
+
+template <int MT, int MODE>
+__global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
+  constexpr int NT = MT == 0 ? 1 : Cfg<MT>::NT;
+  constexpr int kRed = MT == 0 ? 1 : (kWaves - 1) * MT * NT * 4 * kWave;
+  __shared__ float red[kRed];
+  __shared__ int lds_item;
+  __shared__ int lds_flag;
+  __shared__ int lds_am[VG_MAX_M_DEV];
+  Best<MT == 0 ? 1 : MT * 4> best;
+  best.init();
+
+  if constexpr (MODE == MODE_DIRECT) {
+    auto nodep = [] { return true; };
+    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, best);
+    return;
+  } else {
+    StreamCtl* ctl = a.ctl;
+    int cur = 0;  // job cursor (tickets only grow)
+    int done_stage = -1;
+    for (int step = 0;; ++step) {
+      int t;
+      if constexpr (MODE == MODE_GRID) {
+        t = blockIdx.x + step * gridDim.x;
+      } else {
+        if (threadIdx.x == 0)
+          lds_item = (int)__hip_atomic_fetch_add(&ctl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        t = lds_item;
+        __syncthreads();
+      }
+      if (t >= a.total_items) break;
+      const StreamJob* jp;
+      if constexpr (MODE == MODE_GRID) {
+        jp = &a.job0;
+      } else {
+        while (cur + 1 < a.njobs && a.jobs[cur + 1].item_begin <= t) ++cur;
+        jp = &a.jobs[cur];
+      }
+      const StreamJob j = *jp;
+      const int item = t - j.item_begin;
+      // the stage dependency: every item of the previous stage finished
+      auto dep = [&]() -> bool {
+        if constexpr (MODE == MODE_TICKET) {
+          const int need = j.stage - 1;
+          if (need > done_stage) {
+            if (threadIdx.x == 0) lds_flag = wait_stage(ctl, need, a.stage_total[need]) ? 1 : 0;
+            __syncthreads();
+            const bool ok = lds_flag != 0;
+            __syncthreads();
+            if (!ok) return false;
+            done_stage = need;
+          }
+        }
+        return true;
+      };
+      run_item<MT>(j, item, a.M, dep, red, best);
+      if constexpr (MODE == MODE_TICKET) {
+        // Outputs are stored with agent-coherent (write-through) stores, so
+        // a workgroup-scope release -- every wave's stores complete -- is
+        // enough before the relaxed count; no L2 write-back is needed.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        if (threadIdx.x == 0)
+          __hip_atomic_fetch_add(&ctl->stage_done[j.stage], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (a.has_lmhead) publish<MT>(ctl, a.M, best);
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(&ctl->exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      lds_flag = prev == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!lds_flag) return;
+    __threadfence();
+    finish_lmhead(ctl, a, lds_am);
+  }
+}
+
+int num_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int MT, int MODE>
+int resident_blocks() {
+  static int per_cu = 0;
+  if (!per_cu) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<MT, MODE>, kWG, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  return per_cu * num_cus();
+}
+
+template <int MT>
+hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
+  switch (mode) {
+    case MODE_DIRECT:
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_DIRECT>), dim3(grid), dim3(kWG), 0, stream, a);
+      break;
+    case MODE_GRID: {
+      const int cap = resident_blocks<MT, MODE_GRID>();
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_GRID>), dim3(grid < cap ? grid : cap), dim3(kWG), 0, stream, a);
+      break;
+    }
+    default: {
+      // One workgroup per CU: measured, more resident workgroups only park
+      // more prefetched items behind the stage barriers and lengthen the
+      // memory queue the last items of a stage wait in.
+      int cap = resident_blocks<MT, MODE_TICKET>();
+      if (cap > num_cus()) cap = num_cus();
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_TICKET>), dim3(grid < cap ? grid : cap), dim3(kWG), 0, stream, a);
+      break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int stream_mt_class(int M) { return M == 1 ? 0 : (M + 15) / 16; }
+
+int stream_rows_per_item(int M, int K) {
+  const int mt = stream_mt_class(M);
+  if (mt == 0) {
+    if (K == 5120) return GemvItem<5, 4>::kRows;
+    if (K == 17408) return GemvItem<17, 1>::kRows;
+    if (K == 1024) return GemvItem<1, 8>::kRows;
+    return GemvGenericItem::kRows;
+  }
+  return 16 * (mt <= 2 ? 2 : 4);
+}
+
+hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
+  switch (stream_mt_class(a.M)) {
+    case 0: return launch_mt<0>(a, mode, grid, stream);
+    case 1: return launch_mt<1>(a, mode, grid, stream);
+    case 2: return launch_mt<2>(a, mode, grid, stream);
+    case 3: return launch_mt<3>(a, mode, grid, stream);
+    case 4: return launch_mt<4>(a, mode, grid, stream);
+    case 5: return launch_mt<5>(a, mode, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vg

@@ -6,16 +6,15 @@ lm_head (248,320 x 5120) with its fused argmax and greedy accept -- 449
 matrices, 14,115,962,880 weight bytes.  The pages capture each decode step
 as one graph so host launch cost disappears (ling-engine README, "Six
 levers"; the veloGB10 docs list a switch to turn the decode graphs off);
-here the 449 launches go through the C ABI on one stream, in the per-layer
-order {q, k, v} -> o -> {gate, up} -> down, and are captured once into a HIP
-graph and replayed.
+on MI355X the whole step is ONE persistent launch of the native step
+executor (vg_pass_run), which streams the 449 matrices in the per-layer
+dependency order {q, k, v} -> o -> {gate, up} -> down with device-side stage
+barriers.  The one-launch-per-matrix schedule is kept for comparison.
 
-This module only sequences launches: it holds device buffers and precomputed
-pointers and calls libvgemm.so.  All arithmetic is in the HIP kernels.
+This module only holds device buffers and describes the jobs; all
+sequencing and arithmetic happen in libvgemm.so.
 """
 from __future__ import annotations
-
-import ctypes
 
 import torch
 
@@ -55,9 +54,10 @@ class PassWeights:
 
 
 class PassRun:
-    """Activations, outputs and workspaces for one batch size M on top of
-    shared PassWeights; ``launch()`` enqueues the whole pass on the current
-    stream, ``capture()`` records it into a graph."""
+    """Activations, outputs and the lm_head buffers for one batch size M on
+    top of shared PassWeights, and the step itself as a native vg_pass:
+    ``run()`` is one persistent launch of the whole step, ``run_unfused()``
+    the same work as one launch per matrix."""
 
     def __init__(self, weights: PassWeights, M: int, T: int | None = None, x_seed: int = 77):
         if T is None:
@@ -65,25 +65,16 @@ class PassRun:
         self.w = weights
         self.M, self.T = M, T
         dev = weights.device
-        lib = binding.load()
-        self.lib = lib
         self.x = {k: synth.gen_x_device(M, k, x_seed * 10 + k, dev) for k in (HIDDEN, MLP)}
         self.y = []
-        self.calls = []
-        self.workspaces = {}
+        gemms = []
+        # stages: {q,k,v} -> o -> {gate,up} -> down per layer
+        stage_of = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
         for m in weights.mats:
-            n, k = m["n"], m["k"]
-            y = torch.empty((M, n), dtype=torch.float32, device=dev)
+            y = torch.empty((M, m["n"]), dtype=torch.float32, device=dev)
             self.y.append(y)
-            wsb = lib.vg_gemm_workspace_bytes(M, n, k)
-            key = (n, k)
-            if wsb and key not in self.workspaces:
-                self.workspaces[key] = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-            wsp = self.workspaces.get(key)
-            self.calls.append((self.x[k].data_ptr(), m["wq"].data_ptr(), m["ws"].data_ptr(),
-                               ctypes.c_float(m["g"]), M, n, k, y.data_ptr(),
-                               wsp.data_ptr() if wsp is not None else None,
-                               wsp.numel() if wsp is not None else 0))
+            gemms.append((self.x[m["k"]], m["wq"], m["ws"], m["g"], y,
+                          4 * m["layer"] + stage_of[m["name"]]))
         S = M // T
         gen = torch.Generator(device=dev)
         gen.manual_seed(x_seed)
@@ -91,40 +82,35 @@ class PassRun:
                                     device=dev, generator=gen)[:, :T - 1].contiguous()
         self.argmax = torch.empty(M, dtype=torch.int32, device=dev)
         self.accept_len = torch.empty(S, dtype=torch.int32, device=dev)
-        self.lm_ws = torch.zeros(lib.vg_lmhead_workspace_bytes(M), dtype=torch.uint8, device=dev)
         lm = weights.lmhead
-        self.lm_call = (self.x[HIDDEN].data_ptr(), lm["wq"].data_ptr(), lm["ws"].data_ptr(),
-                        ctypes.c_float(lm["g"]), self.drafts.data_ptr() if T > 1 else None,
-                        M, HIDDEN, weights.vocab, T, self.argmax.data_ptr(),
-                        self.accept_len.data_ptr(), self.lm_ws.data_ptr(), self.lm_ws.numel())
+        self.step = binding.Pass(gemms, M, (self.x[HIDDEN], lm["wq"], lm["ws"], lm["g"], T,
+                                            self.drafts, self.argmax, self.accept_len))
         self.graph = None
 
     def set_drafts(self, drafts: torch.Tensor):
         self.drafts.copy_(drafts)
 
-    def launch(self, stream=None):
-        s = int((stream or torch.cuda.current_stream()).cuda_stream)
-        f = self.lib.nvfp4_gemm_ex
-        for c in self.calls:
-            st = f(*c, s)
-            if st:
-                raise binding.VgemmError(st, "nvfp4_gemm_ex")
-        st = self.lib.lmhead_argmax_accept_ex(*self.lm_call, s)
-        if st:
-            raise binding.VgemmError(st, "lmhead_argmax_accept_ex")
+    def run(self, stream=None):
+        self.step.run(stream)
 
-    def capture(self) -> torch.cuda.CUDAGraph:
-        # one eager pass first so every lazily initialised resource exists
-        self.launch()
+    def run_unfused(self, stream=None):
+        self.step.run_unfused(stream)
+
+    def capture_unfused(self) -> torch.cuda.CUDAGraph:
+        """The one-launch-per-matrix schedule captured into a graph."""
+        self.run_unfused()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
-                self.launch()
+                self.run_unfused()
         torch.cuda.synchronize()
         self.graph = g
         return g
 
-    def replay(self):
-        self.graph.replay()
+    def check(self) -> int:
+        return self.step.check()
+
+    def close(self):
+        self.step.close()
