@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvgemm.so")
-SOURCES = ["api.cpp", "stream.hip", "bwprobe.hip"]
+SOURCES = ["api.cpp", "stream.hip", "step_gemv.hip", "bwprobe.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code: hipcc may form
@@ -22,7 +22,7 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
+    "-Wno-unused-result", "-Wno-inline-asm", "-I", os.path.join(ROOT, "include"),
 ]
 
 

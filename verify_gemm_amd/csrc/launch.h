@@ -31,26 +31,36 @@ struct StreamJob {
   int pad;
 };
 
-// Device-side control block of a streaming launch.  It must be zero before
-// the first launch; every launch leaves it zero again (the last workgroup
-// out resets it), except `error`, which stays set once a stage wait timed
-// out so the host can see it.
+// Device-side control block of a launch that has an lm_head (argmax keys)
+// or waits on stages.  It must be zero before the first launch; every
+// launch leaves it zero again (the last workgroup out resets it), except
+// `error`, which stays set once a stage wait timed out so the host can see it.
 struct StreamCtl {
-  unsigned ticket;
   unsigned exits;
   unsigned error;
-  unsigned pad;
+  unsigned pad[2];
   unsigned long long keys[VG_MAX_M_DEV][kKeySlots];
-  unsigned stage_done[kMaxStages];
+};
+
+// Stage completion counters of a step: each on its own 128-byte line --
+// measured, polling and signalling adjacent counters on one line slows
+// the whole step noticeably.  Zero between launches (reset by the last
+// workgroup out).
+constexpr int kDoneSlots = 8;  // counters per stage, one per XCD
+struct alignas(128) StageCounter {
+  unsigned v;
+  unsigned pad[31];
 };
 
 struct StreamArgs {
-  StreamJob job0;                // the job of a single-job launch
-  const StreamJob* jobs;         // device array (ticket mode)
-  const unsigned* stage_total;   // device array: items per stage (ticket mode)
-  StreamCtl* ctl;                // device control block (grid/ticket modes)
+  StreamJob job0;                // the job of a single-job launch (jobs == nullptr)
+  const StreamJob* jobs;         // device array of a step's jobs
+  const unsigned* stage_total;   // device array: workgroups that signal each stage
+  StageCounter (*stage_done)[kDoneSlots];  // [nstages][kDoneSlots]
+  StreamCtl* ctl;                // control block (lm_head keys, exit count, error)
   int njobs;
   int nstages;
+  int waits;                     // 1: honour stage dependencies (a step)
   int total_items;
   int M;                         // rows of every X
   int T;                         // lm_head rows per sequence
@@ -60,15 +70,28 @@ struct StreamArgs {
   int32_t* accept_len;           // [M/T]
 };
 
-enum StreamMode { STREAM_DIRECT = 0, STREAM_GRID = 1, STREAM_TICKET = 2 };
+enum StreamMode { STREAM_DIRECT = 0, STREAM_GRID = 1, STREAM_STATIC = 2 };
 
 // 0 for the M = 1 path, else the number of 16-row M-tiles.
 int stream_mt_class(int M);
 // Weight rows per item for a batch of M rows and a reduction length K.
 int stream_rows_per_item(int M, int K);
 // DIRECT: grid = items of a.job0.  GRID: a.job0 walked by up to `grid`
-// resident workgroups.  TICKET: the job list, up to `grid` workgroups.
+// resident workgroups.  STATIC: the job list of a step, items assigned
+// round-robin to a grid of co-resident workgroups (at most `grid`).
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream);
+// The exact grid a STATIC launch of a batch of M rows uses (all resident).
+int stream_static_grid(int M);
+
+// M = 1: the whole step (or a single GEMM / lm_head) as one launch of
+// step_gemv_grid() resident workgroups; rows of every job split evenly.
+// Every job's K must satisfy step_gemv_supports (K % 64 == 0, K <= 18432);
+// other M = 1 shapes take the stream kernel.
+// A step launch holds at most kStepMaxJobs jobs (its job table lives in LDS).
+constexpr int kStepMaxJobs = 512;
+hipError_t launch_step_gemv(const StreamArgs& a, hipStream_t stream);
+int step_gemv_grid();
+bool step_gemv_supports(int K);
 
 hipError_t launch_bwprobe(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 size_t bwprobe_sink_floats();

@@ -31,15 +31,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 
 // ---- loads -------------------------------------------------------------
+// Every buffer the kernels touch is global device memory.  Pointers read
+// from a device-side job table carry no address space, and generic (FLAT)
+// accesses would count against the LDS/scalar wait counter too, so every
+// access goes through an explicit global (address space 1) pointer.
+#define VG_GLOBAL __attribute__((address_space(1)))
+
 // Weight bytes are read exactly once per pass: nontemporal (streaming) hint.
-__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
+  return __builtin_nontemporal_load((const VG_GLOBAL u32x4*)p);
+}
 __device__ __forceinline__ unsigned short ld_stream(const unsigned short* p) {
-  return __builtin_nontemporal_load(p);
+  return __builtin_nontemporal_load((const VG_GLOBAL unsigned short*)p);
 }
-__device__ __forceinline__ unsigned ld_stream(const unsigned* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ unsigned ld_stream(const unsigned* p) {
+  return __builtin_nontemporal_load((const VG_GLOBAL unsigned*)p);
+}
 __device__ __forceinline__ unsigned char ld_stream(const unsigned char* p) {
-  return __builtin_nontemporal_load(p);
+  return __builtin_nontemporal_load((const VG_GLOBAL unsigned char*)p);
 }
+// Activations are small and re-read by many workgroups: ordinary cached loads.
+__device__ __forceinline__ u32x4 ld_act(const u32x4* p) { return *(const VG_GLOBAL u32x4*)p; }
 
 // ---- decoding ----------------------------------------------------------
 // Two E4M3 scale bytes (low 16 bits of w) -> two fp32 values.

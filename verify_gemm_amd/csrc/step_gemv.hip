@@ -1,0 +1,684 @@
+// M = 1 (plain decode): the weight stream of a whole step -- or of one GEMM,
+// or of the lm_head pass -- as one launch of one resident workgroup per CU.
+//
+// A decode step reads every weight once and is bound by memory bandwidth
+// (ling-engine README, opening paragraph and "Six levers"; veloGB10 docs,
+// "Engineered to the roofline").  On gfx950 what decides whether a CU keeps
+// its share of HBM bandwidth is how many weight bytes it has in flight at
+// every moment, and the hardware counts a wave's outstanding vector-memory
+// operations with ONE in-order counter (vmcnt) that loads and stores share.
+// A wave that waits for an activation load, or that has a store pending
+// when it waits for a weight load, ends up waiting for everything it issued
+// before -- including the weights prefetched for later work.  So the
+// workgroup is split by role (eight waves, two per SIMD, so that one can
+// compute while the other waits):
+//
+//   * six COMPUTE waves issue nothing but weight loads.  Each walks the
+//     workgroup's chunks with two register buffers: the next chunk's loads
+//     are issued before the current chunk is computed.  Every chunk issues
+//     the same 18 buffer loads per lane in straight-line code; slots a
+//     chunk does not use get an offset past the buffer's range, which the
+//     hardware answers with zeros without touching memory.  So waiting for a
+//     buffer is always exactly "all but the 18 loads issued after it".
+//     Activations and scales are read from LDS, results written to LDS;
+//   * one I/O wave waits for the stage a chunk depends on and copies the
+//     activation row and each chunk's scales into LDS (global-to-LDS DMA,
+//     no registers).  It issues no stores, so its waits for those copies
+//     never include a store round trip;
+//   * one STORE wave stores the results the compute waves left in LDS and
+//     signals a stage once its results are stored and complete.
+//
+// The roles hand over through LDS counters, not barriers: the I/O wave
+// releases chunk k once its activations and scales are in LDS; each
+// compute wave counts the chunks it has finished; the store wave counts
+// the chunks it has stored, which frees the LDS areas they used.  Scales
+// of chunk k+2 go into the area of chunk k-1 (a three-deep ring), results
+// alternate between two areas.
+// Activation rows are double-buffered by "epoch" (a new epoch starts where
+// the stage or the activation pointer changes), so the next stage's row is
+// staged while the last chunk of the current one is still being computed.
+// The job table is copied into LDS at the start, so reading a job
+// descriptor never waits on memory.
+//
+// Work split: every matrix's rows are divided EVENLY over the G workgroups
+// (workgroup w owns rows [N*w/G, N*(w+1)/G) of every matrix), so each
+// dependency stage ({q,k,v} -> o -> {gate,up} -> down per layer, then the
+// lm_head) is balanced to a row; a workgroup's rows of one matrix are cut
+// into equal chunks of at most 8 * (18 / ceil(K/1024)) rows.
+//
+// Arithmetic: half-wave h of a compute wave owns rows 2i + h of the wave's
+// rows; lane L reads 16-byte code pieces L, L+32, ... of the row (512
+// contiguous bytes per half-wave and instruction, nontemporal) and the two
+// E4M3 scales of each piece.  Per 16-element block eight v_dot2_f32_bf16
+// multiply the unscaled E2M1 values (exact in bf16) with X and one FMA
+// applies the block scale; the 32 lanes of a half-wave are summed by a
+// fixed butterfly, so every row is summed in the same order whatever chunk
+// or wave it lands in: results do not depend on the launch.
+//
+// Stage signals: results are stored with agent-coherent stores; the store
+// wave waits until its stores have completed (vmcnt(0)), then adds one to
+// one of eight padded counters of the stage.  A waiter polls the counters,
+// then does an agent-scope acquire before reading activations.  Waits are
+// bounded: on time-out the error flag in the control block is raised and
+// the launch runs on to its end (its results are then invalid).  All
+// workgroups are resident (one per CU), and the stage a chunk waits for
+// only needs chunks that were released before it, so the waits cannot
+// deadlock.
+//
+// lm_head: compute waves keep their best (logit, lowest index) and publish
+// it once at the end; the last workgroup out writes argmax, runs the greedy
+// accept rule (TandemLLM README, introduction; with one row there are no
+// drafts, so accept_len = 0) and zeroes the control block for the next
+// launch.
+#include "launch.h"
+#include "nvfp4_device.h"
+
+namespace vg {
+
+namespace {
+
+constexpr int kCW = 6;                  // compute waves
+constexpr int kIO = kCW;                // index of the I/O wave
+constexpr int kST = kCW + 1;            // index of the store wave
+constexpr int kWG = (kCW + 2) * kWave;  // 512 threads: two waves per SIMD
+constexpr int kSlots = 18;              // 16-byte code pieces per lane per buffer
+constexpr int kMaxK = kSlots * 1024;    // a row of one half-wave fits one buffer
+constexpr int kMaxChunkRows = 2 * kCW * kSlots;
+// Largest scale bytes of one chunk: rows * K/16 <= 2 * kCW * (18 / cpl) * cpl * 64,
+// copied by a fixed number of 1-KB DMA instructions.
+constexpr int kMaxChunkScale = 2 * kCW * kSlots * 64;
+constexpr int kScaleDma = (kMaxChunkScale + 1023) / 1024;
+constexpr int kScaleBufs = 3;  // chunks k, k+1 (ready) and k+2 (in flight)
+constexpr unsigned kOOB = 0x80000000u;  // buffer offset past every range used here
+constexpr int kNT = 2;                  // buffer-load cache policy: nontemporal
+constexpr long kSpinLimit = 1L << 22;   // polls (with sleeps) before giving up
+
+// s_waitcnt immediate for vmcnt(0) (gfx9 encoding: vmcnt[3:0]+[15:14],
+// expcnt[6:4], lgkmcnt[11:8]; the other two fields at "no wait").
+constexpr int kWaitVm0 = 0x0F70;
+// vmcnt(kScaleDma): everything but the newest chunk's scale DMAs.
+constexpr int kWaitVmScale = 0x0F70 | (kScaleDma & 15) | ((kScaleDma >> 4) << 14);
+static_assert(kScaleDma < 64, "vmcnt holds at most 63");
+
+static_assert(sizeof(StreamJob) % 16 == 0, "job descriptors are copied as 16-byte pieces");
+
+__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_out(float* p, float v) {
+  __hip_atomic_store((VG_GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned lds_load(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// The same buffer descriptor as four scalar words, for the DMA below.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, unsigned bytes) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)b);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) & 0xFFFFu;  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// LDS address (byte offset) of a location in LDS.
+template <class T>
+__device__ __forceinline__ unsigned lds_addr(T* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) T*)p;
+}
+
+// One 1-KB global-to-LDS copy: lane i's 16 bytes at byte `voff` of buffer
+// `rs` land at LDS byte lds + 16 * i; an offset past the buffer's range
+// reads nothing.  Written as assembly so that the compiler does not track
+// it: it would otherwise wait for every LDS copy in flight before any LDS
+// read of this wave (including the copies made ahead of time).  Completion
+// is awaited explicitly (vmcnt) by the I/O wave.  The compiler emits no
+// other LDS copy in this kernel, so it keeps nothing in M0 across this.
+// `lds` must be wave-uniform; it is moved to a scalar register here (the
+// "s" constraint alone does not make the compiler move a value that lives
+// in a vector register).
+__device__ __forceinline__ void dma16(u32x4 rs, unsigned voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m)
+               : "memory", "m0");
+}
+
+__host__ __device__ __forceinline__ int pieces_per_lane(int k) { return (k + 1023) >> 10; }
+__host__ __device__ __forceinline__ int chunk_cap(int k) { return 2 * kCW * (kSlots / pieces_per_lane(k)); }
+
+struct Shared {
+  StreamJob jobs[kStepMaxJobs];      // the launch's job table
+  u32x4 xs[2][kMaxK * 2 / 16];       // activation rows of even / odd epochs (bf16)
+  u32x4 sc[kScaleBufs][kScaleDma * 64];  // scale bytes of chunk ordinal k in sc[k % 3]
+  float res[2][kMaxChunkRows];       // results of chunks with even / odd ordinal
+  unsigned done[2];                  // compute waves finished with the chunk of that parity
+  unsigned ready;                    // chunks released to the compute waves
+  unsigned flushed;                  // chunks whose results are stored (all areas they used are free)
+  int flag;
+};
+
+// Job i from the LDS table, in scalar registers.
+__device__ __forceinline__ StreamJob lds_job(const Shared& sh, int i) {
+  struct Words {
+    unsigned w[sizeof(StreamJob) / 4];
+  } v;
+  const unsigned* p = reinterpret_cast<const unsigned*>(&sh.jobs[i]);
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(StreamJob) / 4); ++k) v.w[k] = __builtin_amdgcn_readfirstlane(p[k]);
+  return __builtin_bit_cast(StreamJob, v);
+}
+
+// The code pieces of one chunk, per lane (the chunk's scales are in LDS).
+struct Buf {
+  u32x4 q[kSlots];
+};
+
+struct Chunk {
+  int job, r0, rows;
+};
+
+// Rows [begin, begin + count) of a chunk belong to compute wave w.
+__device__ __forceinline__ void wave_rows(int rows, int w, int& begin, int& count) {
+  begin = rows * w / kCW;
+  count = rows * (w + 1) / kCW - begin;
+}
+
+// Walks this workgroup's chunks in job order (the same in every wave).
+struct Cursor {
+  int job = 0, pos = 0, end = 0, left = 0;  // left: chunks still to cut from [pos, end)
+};
+
+__device__ __forceinline__ bool next_chunk(const Shared& sh, int njobs, Cursor& cu, Chunk& out) {
+  while (cu.left == 0) {
+    if (cu.job >= njobs) return false;
+    const StreamJob j = lds_job(sh, cu.job);
+    const long long G = gridDim.x, w = blockIdx.x;
+    cu.pos = (int)(j.n * w / G);
+    cu.end = (int)(j.n * (w + 1) / G);
+    const int cap = chunk_cap(j.k);
+    cu.left = (cu.end - cu.pos + cap - 1) / cap;
+    if (cu.left == 0) ++cu.job;
+  }
+  const int rows = (cu.end - cu.pos + cu.left - 1) / cu.left;  // near-equal chunks
+  out = Chunk{cu.job, cu.pos, rows};
+  cu.pos += rows;
+  if (--cu.left == 0) ++cu.job;
+  return true;
+}
+
+// Activation epochs: a new one starts where the stage or the activation
+// pointer changes; its row goes to buffer n & 1.  Both roles track them
+// with the same rule.
+struct Epoch {
+  int stage = -1, n = -1;
+  const uint16_t* x = nullptr;
+  __device__ __forceinline__ bool advance(const StreamJob& j) {
+    if (j.stage == stage && j.x == x) return false;
+    stage = j.stage;
+    x = j.x;
+    ++n;
+    return true;
+  }
+};
+
+// ---- compute waves -----------------------------------------------------
+
+// Slot s of the buffer holds piece c = s / rh of local row 2 * (s % rh) + h.
+__device__ __forceinline__ void issue(const StreamJob& j, const Chunk& ch, int w, Buf& b) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, L = lane & 31;
+  int wb, wc;
+  wave_rows(ch.rows, w, wb, wc);
+  const unsigned rb = (unsigned)j.k >> 1;
+  const int cpl = pieces_per_lane(j.k), rh = kSlots / cpl;
+  const size_t row0 = (size_t)(ch.r0 + wb);
+  const __amdgpu_buffer_rsrc_t rw = rsrc(j.wq + row0 * rb, (unsigned)wc * rb);
+  int i = 0, c = 0;
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    const unsigned piece = (unsigned)(L + 32 * c), l = (unsigned)(2 * i + h);
+    const bool ok = c < cpl && (int)l < wc && piece * 16u < rb;
+    b.q[s] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? l * rb + piece * 16u : kOOB, 0, kNT);
+    const bool wrap = i + 1 == rh;
+    i = wrap ? 0 : i + 1;
+    c = wrap ? c + 1 : c;
+  }
+}
+
+// Row sums times g for the wave's rows of a chunk whose rows take RH slots
+// per half-wave (RH = 18 / cpl); pieces c >= cpl are skipped (uniform).
+// Results go to LDS (GEMM) or into this lane's running best (lm_head).
+// Pieces past the end of a row were loaded as zeros and meet zeroed LDS.
+template <int RH>
+__device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch, int w, const Buf& b,
+                                            const unsigned short* sc, float* res, const u32x4* xs,
+                                            float& best_v, int& best_i) {
+  constexpr int CMAX = kSlots / RH;
+  const int lane = threadIdx.x & 63, h = lane >> 5, L = lane & 31;
+  const int cpl = pieces_per_lane(j.k);
+  const int rp = j.k >> 5;  // 16-byte pieces per row = scale pairs per row
+  int wb, wc;
+  wave_rows(ch.rows, w, wb, wc);
+  if (wc == 0) return;
+  float acc[RH];
+#pragma unroll
+  for (int i = 0; i < RH; ++i) acc[i] = 0.0f;
+  // one per-lane base each; every read below adds a constant (immediate)
+  // or a wave-uniform offset to it
+  const u32x4* xl = xs + 4 * L;
+  const unsigned short* sl = sc + (wb + h) * rp + L;
+#pragma unroll
+  for (int c = 0; c < CMAX; ++c) {
+    if (c < cpl) {
+      const u32x4 x0 = xl[128 * c], x1 = xl[128 * c + 1], x2 = xl[128 * c + 2], x3 = xl[128 * c + 3];
+      const bool in_row = L + 32 * c < rp;
+#pragma unroll
+      for (int i = 0; i < RH; ++i) {
+        if (2 * i < wc) {
+          const u32x4 p = b.q[c * RH + i];
+          // the scale pair of this piece; pieces past the row (loaded as
+          // zero codes) take scale 0 so whatever LDS holds there is unused
+          const unsigned short sv = in_row ? sl[2 * i * rp + 32 * c] : (unsigned short)0;
+          const f32x2 s = e4m3x2_lo(sv);
+          acc[i] = block16(p[0], p[1], x0, x1, s[0], acc[i]);
+          acc[i] = block16(p[2], p[3], x2, x3, s[1], acc[i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RH; ++i) {
+    if (2 * i < wc) {
+      const float v = sum_lanes<32>(acc[i]) * j.g;
+      const int l = 2 * i + h;
+      if (L == 0 && l < wc) {
+        const int lr = wb + l;
+        if (j.kind == 0) {
+          res[lr] = v;
+        } else if (better(v, ch.r0 + lr, best_v, best_i)) {
+          best_v = v;
+          best_i = ch.r0 + lr;
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void compute(const StreamJob& j, const Chunk& ch, int w, const Buf& b,
+                                        const unsigned short* sc, float* res, const u32x4* xs,
+                                        float& best_v, int& best_i) {
+  static_assert(kSlots == 18, "the classes below are the values of 18 / cpl");
+  switch (kSlots / pieces_per_lane(j.k)) {
+    case 18: compute_cls<18>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+    case 9: compute_cls<9>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+    case 6: compute_cls<6>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+    case 4: compute_cls<4>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+    case 3: compute_cls<3>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+    case 2: compute_cls<2>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+    default: compute_cls<1>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+  }
+}
+
+__device__ __forceinline__ const unsigned short* scales(const Shared& sh, int idx) {
+  return reinterpret_cast<const unsigned short*>(sh.sc[idx]);
+}
+
+// Waits until chunk ordinal k has been released by the I/O wave (its
+// activations and scales are in LDS).  The I/O wave releases every chunk
+// unless a stage wait timed out, and then it still releases them all.
+__device__ __forceinline__ void wait_ready(const Shared& sh, unsigned k) {
+  while (lds_load(&sh.ready) <= k) __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One released chunk of a compute wave: compute, then report.
+// `sidx` is the chunk's scale area (ordinal % 3).
+__device__ __forceinline__ void work(Shared& sh, const Chunk& ch, int w, const Buf& b, int parity, int& sidx,
+                                     Epoch& ep, float& best_v, int& best_i) {
+  const StreamJob j = lds_job(sh, ch.job);
+  ep.advance(j);
+  compute(j, ch, w, b, scales(sh, sidx), sh.res[parity], sh.xs[ep.n & 1], best_v, best_i);
+  sidx = sidx == kScaleBufs - 1 ? 0 : sidx + 1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");  // results are in LDS
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(&sh.done[parity], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void compute_loop(const StreamArgs& a, Shared& sh, int njobs, float& best_v,
+                                             int& best_i) {
+  // the wave index, known to the compiler as wave-uniform (scalar): buffer
+  // descriptors built from it stay in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Cursor cu;
+  Chunk cur, nxt;
+  Buf b0, b1;
+  Epoch ep;
+  int sidx = 0;
+  unsigned k = 0;  // ordinal of cur
+  // Chunk ordinals alternate parity, and so do the two result areas; with two register buffers, b0 always holds an even chunk and b1
+  // an odd one.  The prefetch is issued even past the last chunk (as an
+  // empty chunk, whose loads are all out of range): every path then has
+  // the same loads outstanding, so the compiler's wait for a buffer is
+  // exactly "all but the 18 loads issued after it".
+  bool have = next_chunk(sh, njobs, cu, cur);
+  if (!have) return;
+  issue(lds_job(sh, cur.job), cur, w, b0);
+  for (;;) {
+    bool more = next_chunk(sh, njobs, cu, nxt);
+    if (!more) nxt = Chunk{cur.job, 0, 0};
+    issue(lds_job(sh, nxt.job), nxt, w, b1);
+    wait_ready(sh, k++);
+    work(sh, cur, w, b0, 0, sidx, ep, best_v, best_i);
+    if (!more) break;
+    cur = nxt;
+    more = next_chunk(sh, njobs, cu, nxt);
+    if (!more) nxt = Chunk{cur.job, 0, 0};
+    issue(lds_job(sh, nxt.job), nxt, w, b0);
+    wait_ready(sh, k++);
+    work(sh, cur, w, b1, 1, sidx, ep, best_v, best_i);
+    if (!more) break;
+    cur = nxt;
+  }
+}
+
+// ---- I/O wave ----------------------------------------------------------
+
+// Polls until `target` workgroups have signalled stage `s` (whole wave,
+// uniform result), then acquires at agent scope.
+__device__ bool wait_stage(const StreamArgs& a, int s, unsigned target) {
+  const int lane = threadIdx.x & 63;
+  for (long it = 0; it < kSpinLimit; ++it) {
+    unsigned v = lane < kDoneSlots ? ld_agent(&a.stage_done[s][lane].v) : 0u;
+#pragma unroll
+    for (int off = kDoneSlots / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    if (__shfl(v, 0, kWave) >= target) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (lane == 0) st_agent(&a.ctl->error, 1u);
+  return false;
+}
+
+// Waits until every compute wave has finished the chunk of `parity`.  The
+// compute waves need nothing more from this wave to finish a released
+// chunk, so the wait ends; it is bounded all the same.
+__device__ bool wait_done(const StreamArgs& a, Shared& sh, int parity) {
+  for (long it = 0; it < kSpinLimit; ++it) {
+    if (__hip_atomic_load(&sh.done[parity], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= (unsigned)kCW) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if ((threadIdx.x & 63) == 0) st_agent(&a.ctl->error, 1u);
+  return false;
+}
+
+// Starts copying the K bf16 activations of job j into `xs` and zeroes the
+// row's pieces past K (up to K rounded up to 1024).  Completes at this
+// wave's vmcnt(0).
+__device__ void stage_x(const StreamJob& j, u32x4* xs) {
+  const int lane = threadIdx.x & 63;
+  const int n16 = j.k >> 3;  // 16-byte pieces of the row
+  const u32x4 rs = rsrc_words(j.x, (unsigned)n16 * 16u);
+  for (int t = 0; t * kWave < n16; ++t)
+    dma16(rs, (unsigned)(t * kWave + lane) * 16u, lds_addr(xs + t * kWave));
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the zeroing below must land after the DMA
+  const int pad16 = pieces_per_lane(j.k) * 128, dma16 = (n16 + kWave - 1) / kWave * kWave;
+  const int end = pad16 > dma16 ? pad16 : dma16;
+  for (int e = n16 + lane; e < end; e += kWave) xs[e] = u32x4{0, 0, 0, 0};
+}
+
+// Starts copying the scale bytes of chunk ch into scale area `idx`
+// (chunk-local row-major, K/16 bytes per row) with exactly kScaleDma DMA
+// instructions (pieces past the chunk are out of range: nothing is read
+// or written for them).  K % 64 == 0 keeps every row's scales whole dwords,
+// so the buffer's range check (per dword) cuts exactly at the matrix's end.
+__device__ void stage_scales(const StreamJob& j, const Chunk& ch, Shared& sh, int idx) {
+  const int lane = threadIdx.x & 63;
+  const unsigned sb = (unsigned)j.k >> 4;
+  const u32x4 rs = rsrc_words(j.ws, (unsigned)j.n * sb);
+  const unsigned base = (unsigned)ch.r0 * sb, bytes = (unsigned)ch.rows * sb;
+#pragma unroll
+  for (int t = 0; t < kScaleDma; ++t) {
+    const unsigned off = (unsigned)(t * kWave + lane) * 16u;
+    dma16(rs, off < bytes ? base + off : kOOB, lds_addr(sh.sc[idx] + t * kWave));
+  }
+}
+
+__device__ void signal_stage(const StreamArgs& a, int s) {
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's result stores have completed
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(&a.stage_done[s][blockIdx.x % kDoneSlots].v, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct IoState {
+  Epoch ep;
+  int done_stage = -1;
+};
+
+// Everything chunk `c` needs before it is released: the stage it depends
+// on, its activation row, and its scales (staged a chunk earlier).  If the
+// newest thing this wave issued is the following chunk's scale DMA
+// (`ahead`), that is all it may leave in flight; otherwise nothing.
+// Loads complete in order, so "at most kScaleDma outstanding" means every
+// load issued before that DMA -- this chunk's scales included -- is done.
+__device__ void prepare(const StreamArgs& a, Shared& sh, const StreamJob& j, IoState& st, bool ahead) {
+  if (j.stage != st.ep.stage && a.waits) {
+    const int need = j.stage - 1;
+    if (need >= 0 && need > st.done_stage) {
+      (void)wait_stage(a, need, a.stage_total[need]);  // a time-out raises the error flag
+      st.done_stage = need;
+    }
+  }
+  if (st.ep.advance(j)) stage_x(j, sh.xs[st.ep.n & 1]);
+  if (ahead)
+    __builtin_amdgcn_s_waitcnt(kWaitVmScale);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+}
+
+// Stores the results of chunk ch (LDS area `parity`) and clears that
+// area's completion count for the chunk after next.
+__device__ void flush(Shared& sh, const StreamJob& j, const Chunk& ch, int parity) {
+  const int lane = threadIdx.x & 63;
+  if (j.kind == 0)
+    for (int t = lane; t < ch.rows; t += kWave) store_out(&j.y[ch.r0 + t], sh.res[parity][t]);
+  if (lane == 0) lds_store(&sh.done[parity], 0u);
+}
+
+// Releases chunk ordinals below `n` to the compute waves.
+__device__ __forceinline__ void release(Shared& sh, unsigned n) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if ((threadIdx.x & 63) == 0) lds_store(&sh.ready, n);
+}
+
+// Waits until the results of chunk ordinals below n are stored.  The store
+// wave needs nothing from this wave for chunks already released.
+__device__ bool wait_flushed(const StreamArgs& a, const Shared& sh, unsigned n) {
+  for (long it = 0; it < kSpinLimit; ++it) {
+    if (lds_load(&sh.flushed) >= n) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if ((threadIdx.x & 63) == 0) st_agent(&a.ctl->error, 1u);
+  return false;
+}
+
+// Per chunk k: once chunk k-1 is stored, the scales of chunk k+2 go into
+// the area chunk k-1 used (a three-deep ring), then chunk k+1 is prepared
+// -- its stage waited for, its activation row staged -- and released.
+// This wave issues nothing but copies into LDS and the stage polls, so its
+// waits never include a store round trip.
+__device__ __forceinline__ void io_loop(const StreamArgs& a, Shared& sh, int njobs) {
+  IoState st;
+  Cursor cu;
+  Chunk cur, nxt, nx2;
+  int sidx = 0;      // scale area of cur
+  unsigned k = 0;    // ordinal of cur
+  if (!next_chunk(sh, njobs, cu, cur)) return;
+  bool more = next_chunk(sh, njobs, cu, nxt);
+  StreamJob cj = lds_job(sh, cur.job), nj = lds_job(sh, more ? nxt.job : cur.job);
+  stage_scales(cj, cur, sh, 0);
+  if (more) stage_scales(nj, nxt, sh, 1);
+  prepare(a, sh, cj, st, false);
+  release(sh, 1);
+  while (more) {
+    const bool more2 = next_chunk(sh, njobs, cu, nx2);
+    // chunk k-1's scale area, result area and activation epoch are free
+    if (k > 0) (void)wait_flushed(a, sh, k);
+    if (more2) {
+      const int s2 = sidx + 2 >= kScaleBufs ? sidx + 2 - kScaleBufs : sidx + 2;
+      stage_scales(lds_job(sh, nx2.job), nx2, sh, s2);
+    }
+    prepare(a, sh, nj, st, more2);
+    release(sh, k + 2);
+    ++k;
+    cur = nxt;
+    cj = nj;
+    nxt = nx2;
+    more = more2;
+    if (more) nj = lds_job(sh, nxt.job);
+    sidx = sidx == kScaleBufs - 1 ? 0 : sidx + 1;
+  }
+}
+
+// ---- store wave --------------------------------------------------------
+
+// Per chunk, once every compute wave has finished it: stores its results
+// and reports it stored; after the last chunk of a stage, waits until its
+// stores are complete and signals the stage.
+__device__ __forceinline__ void store_loop(const StreamArgs& a, Shared& sh, int njobs) {
+  Cursor cu;
+  Chunk cur, nxt;
+  int parity = 0;
+  unsigned k = 0;
+  if (!next_chunk(sh, njobs, cu, cur)) return;
+  for (;;) {
+    const bool more = next_chunk(sh, njobs, cu, nxt);
+    const StreamJob j = lds_job(sh, cur.job);
+    wait_done(a, sh, parity);
+    flush(sh, j, cur, parity);
+    // the LDS reads of the flush have completed before the areas are handed back
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if ((threadIdx.x & 63) == 0) lds_store(&sh.flushed, k + 1);
+    if (a.waits && (!more || lds_job(sh, nxt.job).stage != j.stage)) signal_stage(a, j.stage);
+    if (!more) break;
+    cur = nxt;
+    parity ^= 1;
+    ++k;
+  }
+}
+
+__global__ __launch_bounds__(kWG) void step_gemv_kernel(StreamArgs a) {
+  __shared__ Shared sh;
+  StreamCtl* ctl = a.ctl;
+  // the job table into LDS
+  const int njobs = a.jobs ? a.njobs : 1;
+  if (a.jobs) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.jobs);
+    u32x4* dst = reinterpret_cast<u32x4*>(sh.jobs);
+    for (int i = threadIdx.x; i < njobs * (int)(sizeof(StreamJob) / 16); i += kWG) dst[i] = ld_act(src + i);
+  } else if (threadIdx.x == 0) {
+    sh.jobs[0] = a.job0;
+  }
+  if (threadIdx.x < 2) sh.done[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    sh.ready = 0;
+    sh.flushed = 0;
+  }
+  __syncthreads();
+
+  float best_v = -__builtin_inff();
+  int best_i = -1;
+  const int role = threadIdx.x >> 6;
+  if (role == kIO)
+    io_loop(a, sh, njobs);
+  else if (role == kST)
+    store_loop(a, sh, njobs);
+  else
+    compute_loop(a, sh, njobs, best_v, best_i);
+
+  // A launch that waits on stages or has an lm_head counts its workgroups
+  // out; the last one finishes the lm_head and zeroes the control block and
+  // the stage counters for the next launch.
+  if (!a.waits && !a.has_lmhead) return;
+  if (a.has_lmhead && role < kCW) {
+    // each compute wave publishes its best (the half-waves hold different rows)
+    const float ov = __shfl_xor(best_v, 32, kWave);
+    const int oi = __shfl_xor(best_i, 32, kWave);
+    if (oi >= 0 && (best_i < 0 || better(ov, oi, best_v, best_i))) { best_v = ov; best_i = oi; }
+    if ((threadIdx.x & 63) == 0 && best_i >= 0)
+      __hip_atomic_fetch_max(&ctl->keys[0][blockIdx.x % kKeySlots], argmax_key(best_v, (unsigned)best_i),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(&ctl->exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    sh.flag = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!sh.flag) return;
+  __threadfence();
+  if (threadIdx.x == 0) {
+    if (a.has_lmhead) {
+      unsigned long long best = 0;
+      for (int s = 0; s < kKeySlots; ++s) {
+        const unsigned long long k =
+            __hip_atomic_load(&ctl->keys[0][s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        best = k > best ? k : best;
+        __hip_atomic_store(&ctl->keys[0][s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      a.argmax[0] = (int)key_index(best);
+      a.accept_len[0] = 0;
+    }
+    st_agent(&ctl->exits, 0u);
+  }
+  if (a.waits)
+    for (int s = threadIdx.x; s < a.nstages * kDoneSlots; s += kWG)
+      st_agent(&a.stage_done[s / kDoneSlots][s % kDoneSlots].v, 0u);
+}
+
+int num_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+}  // namespace
+
+bool step_gemv_supports(int K) { return K >= 64 && K % 64 == 0 && K <= kMaxK; }
+
+// One workgroup per CU: the kernel's LDS and registers allow no more, and
+// the stage waits need every workgroup resident.
+int step_gemv_grid() { return num_cus(); }
+
+hipError_t launch_step_gemv(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(step_gemv_kernel, dim3(step_gemv_grid()), dim3(kWG), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace vg

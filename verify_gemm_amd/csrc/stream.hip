@@ -11,16 +11,20 @@
 // weight rows (all of K) handled by one 256-thread workgroup, and a step is
 // one persistent launch that streams items back to back:
 //
-//   * items are handed out in pass order by an atomic ticket.  An item of
-//     stage s (the per-layer order {q,k,v} -> o -> {gate,up} -> down ->
-//     ... -> lm_head) may only consume its activations once every item of
-//     stage s-1 has finished; a workgroup issues the item's weight loads
-//     FIRST (weights never depend on activations) and only then waits on
-//     the stage counter, so HBM keeps streaming across the dependency.
-//     Tickets are taken in order, so every item a waiter depends on is
-//     already held by a running workgroup: no co-residency is assumed and
-//     the wait cannot deadlock (it is bounded anyway and raises an error
-//     flag instead of hanging);
+//   * the step's items are numbered in pass order and dealt round-robin to
+//     a grid of co-resident workgroups (item i to workgroup i mod G), each
+//     working through its items in increasing order.  An item of stage s
+//     (the per-layer order {q,k,v} -> o -> {gate,up} -> down -> ... ->
+//     lm_head) may only consume its activations once stage s-1 is done; a
+//     workgroup issues the item's weight loads FIRST (weights never depend
+//     on activations) and only then waits, so HBM keeps streaming across the
+//     dependency.  Completion is signalled once per workgroup and stage, on
+//     one of eight counters per stage: measured, device-scope atomics on a
+//     single address serialise at several ns each, and a counter per item
+//     plus a ticket per item cost milliseconds per step.  Every workgroup
+//     only waits on stages whose items all precede its own in its order, so
+//     with all workgroups resident the waits cannot deadlock; they are
+//     bounded anyway and raise an error flag instead of hanging;
 //   * M = 1 (plain decode): each half-wave owns a weight row, lane L reads
 //     16-byte chunks L, L+32, ... (512 contiguous bytes per half-wave and
 //     instruction, nontemporal); per 16-block eight v_dot2_f32_bf16 multiply
@@ -66,13 +70,16 @@ __device__ __forceinline__ void st_agent(unsigned* p, unsigned v) {
 // Output stores are agent-coherent (they write through the XCD's L2), so
 // a consumer on another XCD sees them once the producer's count is visible.
 __device__ __forceinline__ void store_out(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((VG_GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 polls until stage `s` has `target` finished items.
-__device__ bool wait_stage(StreamCtl* ctl, int s, unsigned target) {
+// Thread 0 polls until `target` workgroups have signalled stage `s`.
+__device__ bool wait_stage(StageCounter (*sd)[kDoneSlots], StreamCtl* ctl, int s, unsigned target) {
   for (long it = 0; it < kSpinLimit; ++it) {
-    if (ld_agent(&ctl->stage_done[s]) >= target) {
+    unsigned sum = 0;
+#pragma unroll
+    for (int k = 0; k < kDoneSlots; ++k) sum += ld_agent(&sd[s][k].v);
+    if (sum >= target) {
       // agent-scope acquire: drop stale lines so this workgroup's later
       // activation reads see what the previous stage wrote
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -124,7 +131,8 @@ struct GemvItem {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int ch = L + 32 * c;
-      const u32x4 x0 = xp[4 * ch], x1 = xp[4 * ch + 1], x2 = xp[4 * ch + 2], x3 = xp[4 * ch + 3];
+      const u32x4 x0 = ld_act(xp + 4 * ch), x1 = ld_act(xp + 4 * ch + 1);
+      const u32x4 x2 = ld_act(xp + 4 * ch + 2), x3 = ld_act(xp + 4 * ch + 3);
 #pragma unroll
       for (int i = 0; i < RH; ++i) {
         const f32x2 s = e4m3x2_lo(sc[c][i]);
@@ -160,7 +168,7 @@ struct GemvGenericItem {
       const unsigned c0 = ld_stream(cw), c1 = ld_stream(cw + 1);
       const float s = e4m3x2_lo(ld_stream(srow + b))[0];
       const u32x4* xb = reinterpret_cast<const u32x4*>(j.x + 16 * (size_t)b);
-      acc = block16(c0, c1, xb[0], xb[1], s, acc);
+      acc = block16(c0, c1, ld_act(xb), ld_act(xb + 1), s, acc);
     }
     return sum_lanes<64>(acc) * j.g;
   }
@@ -223,7 +231,7 @@ struct MfmaItem {
       const int m = 16 * mt + c;
       const u32x4* xr = reinterpret_cast<const u32x4*>(j.x + (size_t)(m < M ? m : 0) * j.k + e0);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) xa[mt][st] = m < M ? xr[st] : u32x4{0u, 0u, 0u, 0u};
+      for (int st = 0; st < 4; ++st) xa[mt][st] = m < M ? ld_act(xr + st) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -329,7 +337,7 @@ struct MfmaGuardedItem {
         for (int mt = 0; mt < MT; ++mt) {
           const int m = 16 * mt + c;
           u32x4 a = {0u, 0u, 0u, 0u};
-          if (ok && m < M) a = *reinterpret_cast<const u32x4*>(j.x + (size_t)m * j.k + e0);
+          if (ok && m < M) a = ld_act(reinterpret_cast<const u32x4*>(j.x + (size_t)m * j.k + e0));
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b[nt],
@@ -401,9 +409,9 @@ __device__ __forceinline__ void publish_best(StreamCtl* ctl, int m, float v, int
 // MODE_DIRECT: grid = items of one job, no control block (GEMM calls).
 // MODE_GRID:   one job, each workgroup walks items blockIdx.x + i*gridDim.x
 //              (the standalone lm_head pass).
-// MODE_TICKET: the job list of a whole step, items by atomic ticket with
-//              stage waits (the persistent step kernel).
-constexpr int MODE_DIRECT = STREAM_DIRECT, MODE_GRID = STREAM_GRID, MODE_TICKET = STREAM_TICKET;
+// MODE_STATIC: the job list of a whole step, items dealt round-robin to
+//              resident workgroups, with stage waits (the step kernel).
+constexpr int MODE_DIRECT = STREAM_DIRECT, MODE_GRID = STREAM_GRID, MODE_STATIC = STREAM_STATIC;
 
 template <int MT>
 struct Cfg;  // MT = 0: the M = 1 GEMV path
@@ -540,6 +548,21 @@ __device__ __forceinline__ void publish(StreamCtl* ctl, int M, BestT& best) {
   }
 }
 
+// One stage signal from this workgroup.  Outputs are stored with
+// agent-coherent (write-through) stores; each wave first waits until its
+// own stores have completed (vmcnt(0) -- a workgroup-scope fence does not
+// wait for global stores), so after the barrier every output of the stage
+// is visible at agent scope before the counter moves.  No L2 write-back is
+// needed.  Called by the whole workgroup at a point where no weight loads
+// are in flight.
+__device__ void signal_stage(const StreamArgs& a, int s) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(&a.stage_done[s][blockIdx.x % kDoneSlots].v, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The last workgroup out: argmax from the key slots, greedy accept, reset.
 __device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am) {
   const int tid = threadIdx.x;
@@ -565,11 +588,10 @@ __device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am) 
       a.accept_len[q] = L;
     }
   }
-  for (int s = tid; s < a.nstages; s += kWG) st_agent(&ctl->stage_done[s], 0u);
-  if (tid == 0) {
-    st_agent(&ctl->ticket, 0u);
-    st_agent(&ctl->exits, 0u);
-  }
+  if (a.waits)
+    for (int s = tid; s < a.nstages * kDoneSlots; s += kWG)
+      st_agent(&a.stage_done[s / kDoneSlots][s % kDoneSlots].v, 0u);
+  if (tid == 0) st_agent(&ctl->exits, 0u);
 }
 
 template <int MT, int MODE>
@@ -577,7 +599,6 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
   constexpr int NT = MT == 0 ? 1 : Cfg<MT>::NT;
   constexpr int kRed = MT == 0 ? 1 : (kWaves - 1) * MT * NT * 4 * kWave;
   __shared__ float red[kRed];
-  __shared__ int lds_item;
   __shared__ int lds_flag;
   __shared__ int lds_am[VG_MAX_M_DEV];
   Best<MT == 0 ? 1 : MT * 4> best;
@@ -589,20 +610,11 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
     return;
   } else {
     StreamCtl* ctl = a.ctl;
-    int cur = 0;  // job cursor (tickets only grow)
-    int done_stage = -1;
-    for (int step = 0;; ++step) {
-      int t;
-      if constexpr (MODE == MODE_GRID) {
-        t = blockIdx.x + step * gridDim.x;
-      } else {
-        if (threadIdx.x == 0)
-          lds_item = (int)__hip_atomic_fetch_add(&ctl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        t = lds_item;
-        __syncthreads();
-      }
-      if (t >= a.total_items) break;
+    const int G = gridDim.x;
+    int cur = 0;          // job cursor (items only grow)
+    int done_stage = -1;  // highest stage known complete
+    int my_stage = -1;    // stage of the items this workgroup is working on
+    for (int t = blockIdx.x; t < a.total_items; t += G) {
       const StreamJob* jp;
       if constexpr (MODE == MODE_GRID) {
         jp = &a.job0;
@@ -612,12 +624,19 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
       }
       const StreamJob j = *jp;
       const int item = t - j.item_begin;
-      // the stage dependency: every item of the previous stage finished
+      if constexpr (MODE == MODE_STATIC) {
+        if (j.stage != my_stage) {
+          // leaving a stage: one signal for all of this workgroup's items in it
+          if (my_stage >= 0) signal_stage(a, my_stage);
+          my_stage = j.stage;
+        }
+      }
+      // the stage dependency: every workgroup holding items of stage s-1 is done
       auto dep = [&]() -> bool {
-        if constexpr (MODE == MODE_TICKET) {
+        if constexpr (MODE == MODE_STATIC) {
           const int need = j.stage - 1;
           if (need > done_stage) {
-            if (threadIdx.x == 0) lds_flag = wait_stage(ctl, need, a.stage_total[need]) ? 1 : 0;
+            if (threadIdx.x == 0) lds_flag = wait_stage(a.stage_done, ctl, need, a.stage_total[need]) ? 1 : 0;
             __syncthreads();
             const bool ok = lds_flag != 0;
             __syncthreads();
@@ -628,15 +647,10 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
         return true;
       };
       run_item<MT>(j, item, a.M, dep, red, best);
-      if constexpr (MODE == MODE_TICKET) {
-        // Outputs are stored with agent-coherent (write-through) stores, so
-        // a workgroup-scope release -- every wave's stores complete -- is
-        // enough before the relaxed count; no L2 write-back is needed.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __syncthreads();
-        if (threadIdx.x == 0)
-          __hip_atomic_fetch_add(&ctl->stage_done[j.stage], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if constexpr (MODE == MODE_STATIC) __syncthreads();  // LDS reuse by the next item
+    }
+    if constexpr (MODE == MODE_STATIC) {
+      if (my_stage >= 0) signal_stage(a, my_stage);
     }
     if (a.has_lmhead) publish<MT>(ctl, a.M, best);
     __threadfence();
@@ -686,15 +700,10 @@ hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream
       hipLaunchKernelGGL((stream_kernel<MT, MODE_GRID>), dim3(grid < cap ? grid : cap), dim3(kWG), 0, stream, a);
       break;
     }
-    default: {
-      // One workgroup per CU: measured, more resident workgroups only park
-      // more prefetched items behind the stage barriers and lengthen the
-      // memory queue the last items of a stage wait in.
-      int cap = resident_blocks<MT, MODE_TICKET>();
-      if (cap > num_cus()) cap = num_cus();
-      hipLaunchKernelGGL((stream_kernel<MT, MODE_TICKET>), dim3(grid < cap ? grid : cap), dim3(kWG), 0, stream, a);
+    default:
+      // exactly stream_static_grid(M) workgroups: the stage targets count them
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_STATIC>), dim3(grid), dim3(kWG), 0, stream, a);
       break;
-    }
   }
   return hipGetLastError();
 }
@@ -712,6 +721,22 @@ int stream_rows_per_item(int M, int K) {
     return GemvGenericItem::kRows;
   }
   return 16 * (mt <= 2 ? 2 : 4);
+}
+
+int stream_static_grid(int M) {
+  // All workgroups must be resident (the static schedule waits on them);
+  // one per CU measured best: more only park more prefetched items behind
+  // the stage waits.
+  int cap = 0;
+  switch (stream_mt_class(M)) {
+    case 0: cap = resident_blocks<0, MODE_STATIC>(); break;
+    case 1: cap = resident_blocks<1, MODE_STATIC>(); break;
+    case 2: cap = resident_blocks<2, MODE_STATIC>(); break;
+    case 3: cap = resident_blocks<3, MODE_STATIC>(); break;
+    case 4: cap = resident_blocks<4, MODE_STATIC>(); break;
+    default: cap = resident_blocks<5, MODE_STATIC>(); break;
+  }
+  return cap < num_cus() ? cap : num_cus();
 }
 
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
