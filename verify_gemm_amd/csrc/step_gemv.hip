@@ -257,10 +257,20 @@ __device__ __forceinline__ void issue(const StreamJob& j, const Chunk& ch, int w
   }
 }
 
+// sum_{j<16} x_j * e_j for one 16-element block (codes c0, c1; activations
+// xa, xb) as two independent four-deep dot2 chains; with several rows and
+// blocks per piece a wave keeps many independent chains in flight.
+__device__ __forceinline__ float block_dot(unsigned c0, unsigned c1, u32x4 xa, u32x4 xb) {
+  return dot8(c0, xa, 0.0f) + dot8(c1, xb, 0.0f);
+}
+
 // Row sums times g for the wave's rows of a chunk whose rows take RH slots
 // per half-wave (RH = 18 / cpl); pieces c >= cpl are skipped (uniform).
-// Results go to LDS (GEMM) or into this lane's running best (lm_head).
-// Pieces past the end of a row were loaded as zeros and meet zeroed LDS.
+// Every slot of a present piece is computed without a branch: slots of
+// rows the wave does not have hold zero codes (their loads were out of
+// range) and their sums are never used.  Results go to LDS (GEMM) or into
+// this lane's running best (lm_head).  Pieces past the end of a row were
+// loaded as zeros and meet zeroed LDS.
 template <int RH>
 __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch, int w, const Buf& b,
                                             const unsigned short* sc, float* res, const u32x4* xs,
@@ -286,15 +296,13 @@ __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch,
       const bool in_row = L + 32 * c < rp;
 #pragma unroll
       for (int i = 0; i < RH; ++i) {
-        if (2 * i < wc) {
-          const u32x4 p = b.q[c * RH + i];
-          // the scale pair of this piece; pieces past the row (loaded as
-          // zero codes) take scale 0 so whatever LDS holds there is unused
-          const unsigned short sv = in_row ? sl[2 * i * rp + 32 * c] : (unsigned short)0;
-          const f32x2 s = e4m3x2_lo(sv);
-          acc[i] = block16(p[0], p[1], x0, x1, s[0], acc[i]);
-          acc[i] = block16(p[2], p[3], x2, x3, s[1], acc[i]);
-        }
+        const u32x4 p = b.q[c * RH + i];
+        // the scale pair of this piece; pieces past the row (loaded as
+        // zero codes) take scale 0 so whatever LDS holds there is unused
+        const unsigned short sv = in_row ? sl[2 * i * rp + 32 * c] : (unsigned short)0;
+        const f32x2 s = e4m3x2_lo(sv);
+        acc[i] = __builtin_fmaf(s[0], block_dot(p[0], p[1], x0, x1), acc[i]);
+        acc[i] = __builtin_fmaf(s[1], block_dot(p[2], p[3], x2, x3), acc[i]);
       }
     }
   }
