@@ -15,8 +15,11 @@ Also measured in the same run:
   * ``roofline``: the dominant kernel is the step kernel itself (the whole
     pass is one launch): 14,115,962,880 weight bytes per launch over its
     event-timed average duration at the first M;
-  * the CPU oracle on a bounded sample (layer 0's seven matrices at M = 1)
-    on this host's cores -> ``cpu_baseline``.
+  * ``roofline.traffic``: HBM bytes per launch of that kernel from the
+    committed rocprofv3 counter summary (profiles/), null once the kernel
+    sources differ from the ones the counters were taken with;
+  * the CPU oracle on a bounded sample (whole layers at M = 1, about 12 s
+    of oracle time) on this host's cores -> ``cpu_baseline``.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--ms 1,4,17,68]
 """
@@ -41,6 +44,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     return ap.parse_args()
+
+
+def step_kernel_name(M: int) -> str:
+    """The kernel one step launch runs: the M = 1 step kernel, else the
+    static-schedule stream kernel (every job of the pass has K % 64 == 0
+    and K <= 18432, so M = 1 always takes the step kernel)."""
+    return "step_gemv_kernel" if M == 1 else f"stream_kernel<{(M + 15) // 16}, 2>"
 
 
 def log(msg):
@@ -76,29 +86,51 @@ def bwprobe(device, gib=8, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(weights):
-    """The CPU oracle, untuned, on layer 0's seven matrices at M = 1."""
+def blas_threads() -> int:
+    """Threads the oracle's BLAS calls run on (what numpy's library reports)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:  # noqa: BLE001 - the count is informational
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(weights, budget_s: float = 12.0, max_layers: int = 16):
+    """The CPU oracle, untuned, at M = 1 on whole layers (q, k, v, o, gate,
+    up, down) in order, until about `budget_s` seconds of CPU work."""
     import numpy as np
 
     import oracle
     from verify_gemm_amd import synth
-    cores = len(os.sched_getaffinity(0))
-    mats = [m for m in weights.mats if m["layer"] == 0]
-    host = []
-    nbytes = 0
-    for m in mats:
-        host.append((m["wq"].cpu().numpy(), m["ws"].cpu().numpy(), m["g"], m["k"]))
-        nbytes += m["wq"].numel() + m["ws"].numel()
     rng = np.random.default_rng(5)
     xs = {k: synth.gen_x(rng, 1, k, 0.1) for k in (synth.HIDDEN, synth.MLP)}
-    t0 = time.perf_counter()
-    for wq, ws, g, k in host:
-        oracle.nvfp4_gemm_ref(xs[k], wq, ws, g, with_bound=False)
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"layer 0 (q,k,v,o,gate,up,down; {nbytes} weight bytes) at M=1 through the fp64 "
-                      f"numpy oracle (no bounds) in {dt:.2f} s; a full pass is {PASS_WEIGHT_BYTES / nbytes:.1f}x "
-                      f"this sample (~{dt * PASS_WEIGHT_BYTES / nbytes:.0f} s on these cores)"}
+    nbytes, dt, layers = 0, 0.0, 0
+    while layers < max_layers and dt < budget_s:
+        for m in (m for m in weights.mats if m["layer"] == layers):
+            wq, ws = m["wq"].cpu().numpy(), m["ws"].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.nvfp4_gemm_ref(xs[m["k"]], wq, ws, m["g"], with_bound=False)
+            dt += time.perf_counter() - t0
+            nbytes += wq.size + ws.size
+        layers += 1
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"layers 0-{layers - 1} (q,k,v,o,gate,up,down; {nbytes} weight bytes) at M=1 through the "
+                      f"fp64 numpy oracle (no error bounds) in {dt:.1f} s of oracle time; a full pass is "
+                      f"{PASS_WEIGHT_BYTES / nbytes:.1f}x this sample (~{dt * PASS_WEIGHT_BYTES / nbytes:.0f} s)"}
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when it is missing or the kernel sources changed since."""
+    from verify_gemm_amd import profile_summary
+    rec = profile_summary.recorded_traffic(
+        os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "step_kernels_full_pass_hbm_traffic.md"))
+    if rec is None:
+        return None
+    return rec["traffic_bytes"].get(kernel)
 
 
 def main():
@@ -168,8 +200,10 @@ def main():
         "per_m": per_m,
         "bwprobe_read_gbps": round(probe, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": f"stream_kernel (the whole step, one launch) at M={ms_list[0]}",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": recorded_traffic(step_kernel_name(ms_list[0])),
+                     "kernel": (f"{step_kernel_name(ms_list[0])} (the whole step is one launch of it) "
+                                f"at M={ms_list[0]}"),
                      "avg_us": kus, "bytes_per_launch": wbytes},
     }
     if not args.no_cpu_baseline:

@@ -1,0 +1,140 @@
+"""Short text summaries of rocprofv3 output for the profiles/ folder.
+
+Two summaries, each written as Markdown with the exact commands that
+produced its input:
+
+  * ``trace``: the ``--kernel-trace --stats`` kernel statistics of a bench
+    run, restricted to this library's kernels and the reference kernels of
+    known size (the read probe, torch's fill);
+  * ``pmc``: per-dispatch ``FETCH_SIZE`` and ``WRITE_SIZE`` (two separate
+    counter runs) for the same kernels, the scale factors derived from the
+    kernels of known size (the probe reads exactly its buffer, torch's fill
+    writes exactly its buffer), and the resulting HBM traffic per launch of
+    each step kernel.  It also records a hash of the kernel sources the
+    counters were taken with: bench.py reports the traffic only while the
+    sources still hash the same.
+
+    python -m verify_gemm_amd.profile_summary trace STATS_CSV CMD OUT
+    python -m verify_gemm_amd.profile_summary pmc FETCH_CSV WRITE_CSV CMD_F CMD_W PROBE_BYTES FILL_BYTES OUT
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+# Sources whose change invalidates recorded counter values.
+KERNEL_SOURCES = ["csrc/step_gemv.hip", "csrc/stream.hip", "csrc/nvfp4_device.h", "csrc/launch.h"]
+PASS_WEIGHT_BYTES = 14115962880
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str | None:
+    if "step_gemv_kernel" in name:
+        return "step_gemv_kernel"
+    if "stream_kernel<" in name:
+        return "stream_kernel<" + name.split("stream_kernel<", 1)[1].split(">", 1)[0] + ">"
+    if "bwprobe_kernel" in name:
+        return "bwprobe_kernel (read probe)"
+    if "FillFunctor" in name:
+        return "torch fill (write reference)"
+    return None
+
+
+def trace(stats_csv: str, cmd: str, out: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel trace: full-pass step kernels", "", "Command (run from /tmp, `TMPDIR=/tmp`):", "",
+             "```", cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        n = short_name(r["Name"])
+        if n is None:
+            continue
+        lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    lines += ["", "step_gemv_kernel is one launch per M = 1 pass; stream_kernel<2, 2> (two 16-row M-tiles, "
+              "static schedule) is one launch per M = 17 pass.", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+
+
+def _per_dispatch(path: str, counter: str):
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        n = short_name(r["Kernel_Name"])
+        if n is not None and r["Counter_Name"] == counter:
+            agg[n].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()}
+
+
+def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int, fill_bytes: int,
+        out: str) -> None:
+    fetch, nf = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, nw = _per_dispatch(write_csv, "WRITE_SIZE")
+    f_scale = probe_bytes / (fetch["bwprobe_kernel (read probe)"] * 1024)
+    w_scale = fill_bytes / (write["torch fill (write reference)"] * 1024)
+    traffic = {}
+    for k in sorted(set(fetch) | set(write)):
+        if k.startswith("step_gemv") or k.startswith("stream_kernel"):
+            traffic[k] = round(fetch.get(k, 0) * 1024 * f_scale + write.get(k, 0) * 1024 * w_scale)
+    lines = ["# HBM traffic of the step kernels (rocprofv3 counters)", "",
+             "Two counter runs (run from /tmp, `TMPDIR=/tmp`):", "", "```", cmd_f, cmd_w, "```", "",
+             "| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |",
+             "|---|---:|---:|---:|"]
+    for k in sorted(set(fetch) | set(write)):
+        lines.append(f"| {k} | {nf.get(k, 0)} | {fetch.get(k, 0):.6g} | {write.get(k, 0):.6g} |")
+    lines += ["", f"Scale factors from the kernels of known size: reads x{f_scale:.4f} "
+              f"(the probe reads {probe_bytes} bytes per dispatch), writes x{w_scale:.4f} "
+              f"(torch's fill writes {fill_bytes} bytes per dispatch).", "",
+              "Traffic per launch (scaled fetch + scaled write) against the pass's algorithmic "
+              f"{PASS_WEIGHT_BYTES} weight bytes:", ""]
+    for k, v in traffic.items():
+        lines.append(f"* {k}: {v} bytes ({v / PASS_WEIGHT_BYTES:.3f}x)")
+    record = {"sources_sha256": sources_hash(), "traffic_bytes": traffic,
+              "fetch_scale": f_scale, "write_scale": w_scale}
+    lines += ["", "Machine-readable record (bench.py reads it):", "", "```json", json.dumps(record, indent=1),
+              "```", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+
+
+def recorded_traffic(path: str):
+    """The traffic record of a pmc summary, or None if the summary is
+    missing or the kernel sources changed since it was taken."""
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    try:
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (IndexError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_hash():
+        return None
+    return rec
+
+
+def main(argv):
+    if argv[1] == "trace":
+        trace(argv[2], argv[3], argv[4])
+    elif argv[1] == "pmc":
+        pmc(argv[2], argv[3], argv[4], argv[5], int(argv[6]), int(argv[7]), argv[8])
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv)
