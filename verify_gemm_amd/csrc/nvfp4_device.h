@@ -115,6 +115,20 @@ __device__ __forceinline__ float block16(unsigned c0, unsigned c1, u32x4 xa, u32
 }
 
 // ---- reductions ----------------------------------------------------------
+// Sum over each half-wave (lanes 0-31, 32-63) with DPP moves only (no LDS
+// permute): quad swaps, row rotations by 4 and 8 (every lane of a 16-lane
+// row then holds the row sum), then row_bcast15 adds row 0's sum into row
+// 1 and row 2's into row 3.  The half-wave sums are valid in lanes 16-31
+// and 48-63.  A fixed pattern, so the result is bitwise repeatable.
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  return v;
+}
+
 template <int width>
 __device__ __forceinline__ float sum_lanes(float v) {
 #pragma unroll

@@ -70,6 +70,8 @@
 // accept rule (TandemLLM README, introduction; with one row there are no
 // drafts, so accept_len = 0) and zeroes the control block for the next
 // launch.
+#include <type_traits>
+
 #include "launch.h"
 #include "nvfp4_device.h"
 
@@ -83,7 +85,19 @@ constexpr int kST = kCW + 1;            // index of the store wave
 constexpr int kWG = (kCW + 2) * kWave;  // 512 threads: two waves per SIMD
 constexpr int kSlots = 18;              // 16-byte code pieces per lane per buffer
 constexpr int kMaxK = kSlots * 1024;    // a row of one half-wave fits one buffer
-constexpr int kMaxChunkRows = 2 * kCW * kSlots;
+// Rows per half-wave per chunk: 18 / cpl, capped at 3 -- more rows would
+// need more accumulators than the hot shapes (K = 5120: 3 rows, K = 17408:
+// 1 row) can spare registers for; small K (only in tests) uses 3 of its
+// slots' worth.
+constexpr int kMaxRH = 3;
+constexpr int kMaxChunkRows = 2 * kCW * kMaxRH;
+// An activation row sits in LDS "transposed": a 16-byte unit u = 4q + t
+// (piece q = 32 elements, sub-block t) is stored at t * kXPieces + q, so
+// that the 32 lanes of a half-wave, which read pieces L + 32c, read 512
+// consecutive bytes -- conflict-free -- instead of 16-byte reads at a
+// 64-byte stride, which fall on two of the 32 banks.
+constexpr int kXPieces = kMaxK / 32;
+constexpr int kXRow = 4 * kXPieces;
 // Largest scale bytes of one chunk: rows * K/16 <= 2 * kCW * (18 / cpl) * cpl * 64,
 // copied by a fixed number of 1-KB DMA instructions.
 constexpr int kMaxChunkScale = 2 * kCW * kSlots * 64;
@@ -157,11 +171,28 @@ __device__ __forceinline__ void dma16(u32x4 rs, unsigned voff, unsigned lds) {
 }
 
 __host__ __device__ __forceinline__ int pieces_per_lane(int k) { return (k + 1023) >> 10; }
-__host__ __device__ __forceinline__ int chunk_cap(int k) { return 2 * kCW * (kSlots / pieces_per_lane(k)); }
+__host__ __device__ __forceinline__ int rows_per_half(int k) {
+  const int r = kSlots / pieces_per_lane(k);
+  return r < kMaxRH ? r : kMaxRH;
+}
+__host__ __device__ __forceinline__ int chunk_cap(int k) { return 2 * kCW * rows_per_half(k); }
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time i).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F& f) {
+  static_for_impl<0, N>(f);
+}
 
 struct Shared {
   StreamJob jobs[kStepMaxJobs];      // the launch's job table
-  u32x4 xs[2][kMaxK * 2 / 16];       // activation rows of even / odd epochs (bf16)
+  u32x4 xs[2][kXRow];                // activation rows of even / odd epochs (transposed, see kXPieces)
   u32x4 sc[kScaleBufs][kScaleDma * 64];  // scale bytes of chunk ordinal k in sc[k % 3]
   float res[2][kMaxChunkRows];       // results of chunks with even / odd ordinal
   unsigned done[2];                  // compute waves finished with the chunk of that parity
@@ -242,7 +273,7 @@ __device__ __forceinline__ void issue(const StreamJob& j, const Chunk& ch, int w
   int wb, wc;
   wave_rows(ch.rows, w, wb, wc);
   const unsigned rb = (unsigned)j.k >> 1;
-  const int cpl = pieces_per_lane(j.k), rh = kSlots / cpl;
+  const int cpl = pieces_per_lane(j.k), rh = rows_per_half(j.k);
   const size_t row0 = (size_t)(ch.r0 + wb);
   const __amdgpu_buffer_rsrc_t rw = rsrc(j.wq + row0 * rb, (unsigned)wc * rb);
   int i = 0, c = 0;
@@ -257,20 +288,55 @@ __device__ __forceinline__ void issue(const StreamJob& j, const Chunk& ch, int w
   }
 }
 
-// sum_{j<16} x_j * e_j for one 16-element block (codes c0, c1; activations
-// xa, xb) as two independent four-deep dot2 chains; with several rows and
-// blocks per piece a wave keeps many independent chains in flight.
-__device__ __forceinline__ float block_dot(unsigned c0, unsigned c1, u32x4 xa, u32x4 xb) {
-  return dot8(c0, xa, 0.0f) + dot8(c1, xb, 0.0f);
+// The dot products of G slots are computed as 4*G independent four-deep
+// v_dot2 chains -- one per slot and code word -- interleaved in program
+// order: for each code byte, first the G decodes, then the G dot2s into
+// different chains.  A dependent dot2 then comes 4*G instructions after the
+// previous one on its chain, which hides the decode and dot2 latencies
+// inside one wave; a chain-at-a-time order runs at about a third of the
+// issue rate.  Slot g uses code pieces q[S0 + g * SS] of the buffer and
+// activation set x[XI(g)].  Words 0/1 belong to the piece's first
+// 16-element block, words 2/3 to its second; each block's two chains are
+// added and scaled once.
+template <int G, int S0, int SS, int NX>
+__device__ __forceinline__ void piece_group(const Buf& b, const u32x4 (&x)[NX][4], const f32x2 (&s)[G],
+                                            float (&acc)[G]) {
+  float ch[G][4];
+#pragma unroll
+  for (int sel = 0; sel < 4; ++sel) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x2 e[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const unsigned word = b.q[S0 + g * SS][st];
+        switch (sel) {
+          case 0: e[g] = e2m1x2_bf16<0>(word); break;
+          case 1: e[g] = e2m1x2_bf16<1>(word); break;
+          case 2: e[g] = e2m1x2_bf16<2>(word); break;
+          default: e[g] = e2m1x2_bf16<3>(word); break;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const unsigned xv = x[NX == 1 ? 0 : g][st][sel];
+        ch[g][st] = __builtin_amdgcn_fdot2_f32_bf16(e[g], as_bf16x2(xv), sel == 0 ? 0.0f : ch[g][st], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    acc[g] = __builtin_fmaf(s[g][0], ch[g][0] + ch[g][1], acc[g]);
+    acc[g] = __builtin_fmaf(s[g][1], ch[g][2] + ch[g][3], acc[g]);
+  }
 }
 
 // Row sums times g for the wave's rows of a chunk whose rows take RH slots
-// per half-wave (RH = 18 / cpl); pieces c >= cpl are skipped (uniform).
-// Every slot of a present piece is computed without a branch: slots of
-// rows the wave does not have hold zero codes (their loads were out of
-// range) and their sums are never used.  Results go to LDS (GEMM) or into
-// this lane's running best (lm_head).  Pieces past the end of a row were
-// loaded as zeros and meet zeroed LDS.
+// per half-wave (RH = 18 / cpl).  Slots of rows the wave does not have hold
+// zero codes (their loads were out of range) and their sums are never
+// used.  The rows of one piece form one group (one row: the piece alone);
+// pieces c >= cpl are skipped (uniformly).  Results go to LDS (GEMM) or
+// into this lane's running best (lm_head).
 template <int RH>
 __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch, int w, const Buf& b,
                                             const unsigned short* sc, float* res, const u32x4* xs,
@@ -287,31 +353,61 @@ __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch,
   for (int i = 0; i < RH; ++i) acc[i] = 0.0f;
   // one per-lane base each; every read below adds a constant (immediate)
   // or a wave-uniform offset to it
-  const u32x4* xl = xs + 4 * L;
+  const u32x4* xl = xs + L;
   const unsigned short* sl = sc + (wb + h) * rp + L;
+  auto xpiece = [&](int c, u32x4 (&x)[4]) {
+    x[0] = xl[32 * c];
+    x[1] = xl[kXPieces + 32 * c];
+    x[2] = xl[2 * kXPieces + 32 * c];
+    x[3] = xl[3 * kXPieces + 32 * c];
+  };
+  // the scale pair of piece c of row slot i, read unconditionally (past
+  // the row it reads the next row's scales or the area's slack, still in
+  // the area) and replaced by 0 there: those pieces hold zero codes, and
+  // whatever LDS holds must not meet them
+  auto scale = [&](int c, int i) -> f32x2 {
+    const unsigned short raw = sl[2 * i * rp + 32 * c];
+    return e4m3x2_lo(L + 32 * c < rp ? raw : (unsigned short)0);
+  };
+  // activations double-buffered across pieces: piece c+1's LDS reads are
+  // in flight while piece c is computed
+  u32x4 xb[2][1][4];
+  xpiece(0, xb[0][0]);
+  if constexpr (RH >= 2) {
+    // the RH rows of piece c (slots c*RH + i, one activation set)
+    auto piece = [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      if (c < cpl) {
+        if (c + 1 < CMAX && c + 1 < cpl) xpiece(c + 1, xb[(c + 1) & 1][0]);
+        f32x2 s[RH];
 #pragma unroll
-  for (int c = 0; c < CMAX; ++c) {
-    if (c < cpl) {
-      const u32x4 x0 = xl[128 * c], x1 = xl[128 * c + 1], x2 = xl[128 * c + 2], x3 = xl[128 * c + 3];
-      const bool in_row = L + 32 * c < rp;
-#pragma unroll
-      for (int i = 0; i < RH; ++i) {
-        const u32x4 p = b.q[c * RH + i];
-        // the scale pair of this piece; pieces past the row (loaded as
-        // zero codes) take scale 0 so whatever LDS holds there is unused
-        const unsigned short sv = in_row ? sl[2 * i * rp + 32 * c] : (unsigned short)0;
-        const f32x2 s = e4m3x2_lo(sv);
-        acc[i] = __builtin_fmaf(s[0], block_dot(p[0], p[1], x0, x1), acc[i]);
-        acc[i] = __builtin_fmaf(s[1], block_dot(p[2], p[3], x2, x3), acc[i]);
+        for (int i = 0; i < RH; ++i) s[i] = scale(c, i);
+        piece_group<RH, c * RH, 1, 1>(b, xb[c & 1], s, acc);
       }
-    }
+      // keep later pieces' reads from being hoisted into this one (they
+      // would all be hoisted to the top and spilled)
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<CMAX>(piece);
+  } else {
+    // one row: each piece alone (four chains)
+    auto piece = [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      if (c < cpl) {
+        if (c + 1 < CMAX && c + 1 < cpl) xpiece(c + 1, xb[(c + 1) & 1][0]);
+        const f32x2 s[1] = {scale(c, 0)};
+        piece_group<1, c, 1, 1>(b, xb[c & 1], s, acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<CMAX>(piece);
   }
 #pragma unroll
   for (int i = 0; i < RH; ++i) {
     if (2 * i < wc) {
-      const float v = sum_lanes<32>(acc[i]) * j.g;
+      const float v = half_wave_sum(acc[i]) * j.g;  // valid in lanes L >= 16
       const int l = 2 * i + h;
-      if (L == 0 && l < wc) {
+      if (L == 31 && l < wc) {
         const int lr = wb + l;
         if (j.kind == 0) {
           res[lr] = v;
@@ -327,12 +423,8 @@ __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch,
 __device__ __forceinline__ void compute(const StreamJob& j, const Chunk& ch, int w, const Buf& b,
                                         const unsigned short* sc, float* res, const u32x4* xs,
                                         float& best_v, int& best_i) {
-  static_assert(kSlots == 18, "the classes below are the values of 18 / cpl");
-  switch (kSlots / pieces_per_lane(j.k)) {
-    case 18: compute_cls<18>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
-    case 9: compute_cls<9>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
-    case 6: compute_cls<6>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
-    case 4: compute_cls<4>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
+  static_assert(kMaxRH == 3, "the classes below are the values of rows_per_half");
+  switch (rows_per_half(j.k)) {
     case 3: compute_cls<3>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
     case 2: compute_cls<2>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
     default: compute_cls<1>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
@@ -436,19 +528,26 @@ __device__ bool wait_done(const StreamArgs& a, Shared& sh, int parity) {
   return false;
 }
 
-// Starts copying the K bf16 activations of job j into `xs` and zeroes the
-// row's pieces past K (up to K rounded up to 1024).  Completes at this
+// Starts copying the K bf16 activations of job j into `xs` (transposed,
+// see kXPieces: each copy instruction gathers sub-block t of 64
+// consecutive pieces) and zeroes the pieces past K (up to K rounded up to
+// 1024), which the compute waves read as padding.  Completes at this
 // wave's vmcnt(0).
 __device__ void stage_x(const StreamJob& j, u32x4* xs) {
   const int lane = threadIdx.x & 63;
-  const int n16 = j.k >> 3;  // 16-byte pieces of the row
-  const u32x4 rs = rsrc_words(j.x, (unsigned)n16 * 16u);
-  for (int t = 0; t * kWave < n16; ++t)
-    dma16(rs, (unsigned)(t * kWave + lane) * 16u, lds_addr(xs + t * kWave));
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the zeroing below must land after the DMA
-  const int pad16 = pieces_per_lane(j.k) * 128, dma16 = (n16 + kWave - 1) / kWave * kWave;
-  const int end = pad16 > dma16 ? pad16 : dma16;
-  for (int e = n16 + lane; e < end; e += kWave) xs[e] = u32x4{0, 0, 0, 0};
+  const int pieces = j.k >> 5;
+  const u32x4 rs = rsrc_words(j.x, (unsigned)j.k * 2u);
+  for (int b = 0; b * kWave < pieces; ++b) {
+    const int q = b * kWave + lane;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      dma16(rs, q < pieces ? (unsigned)(4 * q + t) * 16u : kOOB, lds_addr(xs + t * kXPieces + b * kWave));
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the zeroing below must land after the copies
+  const int pad = pieces_per_lane(j.k) * 32;
+  for (int q = pieces + lane; q < pad; q += kWave)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xs[t * kXPieces + q] = u32x4{0, 0, 0, 0};
 }
 
 // Starts copying the scale bytes of chunk ch into scale area `idx`
@@ -633,7 +732,8 @@ __global__ __launch_bounds__(kWG) void step_gemv_kernel(StreamArgs a) {
     const float ov = __shfl_xor(best_v, 32, kWave);
     const int oi = __shfl_xor(best_i, 32, kWave);
     if (oi >= 0 && (best_i < 0 || better(ov, oi, best_v, best_i))) { best_v = ov; best_i = oi; }
-    if ((threadIdx.x & 63) == 0 && best_i >= 0)
+    // the row sums (and so the running bests) live in lanes 31 and 63
+    if ((threadIdx.x & 63) == 31 && best_i >= 0)
       __hip_atomic_fetch_max(&ctl->keys[0][blockIdx.x % kKeySlots], argmax_key(best_v, (unsigned)best_i),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
