@@ -64,8 +64,8 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
             continue
         lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    lines += ["", "step_gemv_kernel is one launch per M = 1 pass; stream_kernel<2, 2> (two 16-row M-tiles, "
-              "static schedule) is one launch per M = 17 pass.", ""]
+    lines += ["", "Each kernel launch is one whole pass: step_gemv_kernel at M = 1; stream_kernel<MT, 2> "
+              "(MT 16-row M-tiles, static schedule) at M >= 2 -- <2, 2> at M = 17, <5, 2> at M = 68.", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
 
