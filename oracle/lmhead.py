@@ -19,6 +19,19 @@ position that draft d[j] fills, so
     accept_len = the largest L <= T-1 with d[j] == argmax[j] for all j < L.
 
 The emitted bonus token is argmax[accept_len]; it is not a separate output.
+
+Tree verify (TandemLLM README, the flow diagram and "The parts": the
+drafters' guesses form a tree, the target verifies the whole tree in one
+pass and keeps the longest path it agrees with): node 0 of a T-node tree is
+the last committed position, node i >= 1 holds drafted token tokens[i-1]
+below parent parents[i-1].  See ``tree_accept_ref``; a chain (parent of
+node i is i-1) is the greedy rule above.
+
+Sliced head (dgx-spark-qwen38 README, opening section: the draft gets the
+target's lm_head cut to 65,536 rows, with a map from rows to token ids):
+head row r stands for token token_map[r]; the argmax is taken over rows
+(lowest row among equal maxima) and reported as its token id, which is
+what drafts are compared with.
 A batch of M = S*T rows holds S independent sequences in contiguous blocks
 of T rows (ling-engine README, "Six levers": several sequences share one
 weight read).
@@ -84,6 +97,60 @@ def accept_len_ref(drafts: np.ndarray, argmax: np.ndarray) -> int:
     return length
 
 
+def tree_accept_ref(tokens: np.ndarray, parents: np.ndarray, argmax: np.ndarray) -> tuple[int, int]:
+    """The longest agreed root path of a draft tree.
+
+    tokens[i-1] and parents[i-1] belong to node i (1 <= i < T); argmax[p]
+    (T entries) is the target's token after node p.  Node i is agreed iff
+    the walk from it to the root only uses valid parents (each in [0, c)
+    for its child c) and every step c -> parent p on the way has
+    tokens[c-1] == argmax[p]; the root is agreed.  Returns (depth, node):
+    the largest number of edges on an agreed node's path, and the lowest
+    such node (0 if only the root is agreed).  The bonus token is
+    argmax[node].  Each node's path is walked on its own (no reuse between
+    nodes), so the definition can be read off directly."""
+    tokens = np.asarray(tokens).reshape(-1)
+    parents = np.asarray(parents).reshape(-1)
+    argmax = np.asarray(argmax).reshape(-1)
+    t = argmax.shape[0]
+    if tokens.shape[0] != t - 1 or parents.shape[0] != t - 1:
+        raise ValueError("need T-1 tokens and T-1 parents for T argmax rows")
+    best_depth, best_node = 0, 0
+    for i in range(1, t):
+        depth, c, agreed = 0, i, True
+        while c != 0:
+            p = int(parents[c - 1])
+            if not (0 <= p < c) or int(tokens[c - 1]) != int(argmax[p]):
+                agreed = False
+                break
+            depth += 1
+            c = p
+        if agreed and depth > best_depth:
+            best_depth, best_node = depth, i
+    return best_depth, best_node
+
+
+def _compared_rows(tokens, parents, argmax) -> list[int]:
+    """Rows whose argmax the tree rule compares with a child's token: every
+    agreed node that is the (valid) parent of some node."""
+    t = argmax.shape[0]
+    rows = set()
+    for i in range(1, t):
+        p = int(parents[i - 1])
+        if 0 <= p < i:
+            # p is agreed iff its own path to the root agrees
+            c, ok = p, True
+            while c != 0:
+                q = int(parents[c - 1])
+                if not (0 <= q < c) or int(tokens[c - 1]) != int(argmax[q]):
+                    ok = False
+                    break
+                c = q
+            if ok:
+                rows.add(p)
+    return sorted(rows)
+
+
 def _row_bound(ax_row: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float, v: int) -> float:
     """Acceptance bound of logit (row, v): one dot product of |x| and |w_v|."""
     w = dequant(wq[v:v + 1], ws[v:v + 1], g)[0]
@@ -92,12 +159,18 @@ def _row_bound(ax_row: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float, v: 
 
 def lmhead_ref(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float,
                T: int, drafts: np.ndarray | None = None, *,
+               token_map: np.ndarray | None = None, parents: np.ndarray | None = None,
                interval: bool = False, row_chunk: int = 4096) -> dict:
     """Run the lm_head verify pass on the CPU.
 
     x_bits uint16[M][K] (bf16 bits), wq uint8[V][K/2], ws uint8[V][K/16],
     g the tensor scale (part of every logit).  M must be a multiple of T;
     drafts int[M/T][T-1] or None (then no accept lengths are computed).
+    token_map int[V] or None: head row r stands for token token_map[r]
+    (``argmax`` then holds token ids, ``argmax_row`` the rows).  parents
+    int[M/T][T-1] or None: drafts are the tokens of a tree (see
+    ``tree_accept_ref``) instead of a chain; then ``accept_node`` is also
+    returned.
 
     Returns a dict with per-row ``argmax`` (int32), ``top1``/``top2`` logits,
     ``idx2``, the bounds ``b1``/``b2`` of the two contenders and
@@ -123,8 +196,10 @@ def lmhead_ref(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float,
     b1 = np.array([_row_bound(ax[r], wq, ws, g, int(i1[r])) for r in range(m)])
     b2 = np.array([_row_bound(ax[r], wq, ws, g, int(i2[r])) if i2[r] >= 0 else 0.0
                    for r in range(m)])
+    ids = i1 if token_map is None else np.asarray(token_map, dtype=np.int64)[i1]
     out = {
-        "argmax": i1.astype(np.int32),
+        "argmax": ids.astype(np.int32),
+        "argmax_row": i1.astype(np.int32),
         "top1": v1, "top2": v2, "idx2": i2.astype(np.int32),
         "b1": b1, "b2": b2,
         "decisive": (v1 - v2) > np.maximum(b1, b2),
@@ -144,12 +219,22 @@ def lmhead_ref(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float,
         s = m // T
         d = np.asarray(drafts, dtype=np.int64).reshape(s, T - 1)
         acc = np.empty(s, dtype=np.int32)
+        node = np.empty(s, dtype=np.int32)
         step_dec = np.empty(s, dtype=bool)
+        par = None if parents is None else np.asarray(parents, dtype=np.int64).reshape(s, T - 1)
         for q in range(s):
             rows_q = slice(q * T, (q + 1) * T)
-            acc[q] = accept_len_ref(d[q], out["argmax"][rows_q])
-            last = min(int(acc[q]), T - 2)
-            step_dec[q] = bool(np.all(out["decisive"][q * T:q * T + last + 1]))
+            am_q = out["argmax"][rows_q]
+            if par is None:
+                acc[q] = accept_len_ref(d[q], am_q)
+                node[q] = acc[q]
+                last = min(int(acc[q]), T - 2)
+                step_dec[q] = bool(np.all(out["decisive"][q * T:q * T + last + 1]))
+            else:
+                acc[q], node[q] = tree_accept_ref(d[q], par[q], am_q)
+                cmp_rows = [q * T + r for r in _compared_rows(d[q], par[q], am_q)]
+                step_dec[q] = bool(np.all(out["decisive"][cmp_rows])) if cmp_rows else True
         out["accept_len"] = acc
+        out["accept_node"] = node
         out["step_decisive"] = step_dec
     return out

@@ -134,3 +134,107 @@ def test_draft_generator_matches_target_with_p():
     d = synth.gen_drafts(rng, am, 1000)
     frac = float(np.mean(d == am[:, :16]))
     assert 0.68 < frac < 0.72
+
+
+# ---- tree verify and the sliced head --------------------------------------
+
+def _agreed_forward(tokens, parents, argmax):
+    """Agreed nodes by forward propagation from the root over child lists
+    (the oracle walks each node up to the root instead)."""
+    t = len(argmax)
+    children = {p: [] for p in range(t)}
+    for i in range(1, t):
+        p = int(parents[i - 1])
+        if 0 <= p < i:
+            children[p].append(i)
+    depth = {0: 0}
+    frontier = [0]
+    while frontier:
+        nxt = []
+        for p in frontier:
+            for c in children[p]:
+                if int(tokens[c - 1]) == int(argmax[p]):
+                    depth[c] = depth[p] + 1
+                    nxt.append(c)
+        frontier = nxt
+    best = max(depth.values())
+    return best, min(n for n, d in depth.items() if d == best)
+
+
+def test_tree_accept_hand_worked():
+    # argmax of node p is the target's token after p
+    am = [10, 20, 30, 40, 50, 60, 70, 80]
+    # node:     1   2   3   4   5   6   7
+    parents = [0, 0, 1, 1, 2, 3, 3]
+    tokens = [10, 11, 20, 99, 30, 41, 40]
+    # 1 agrees (10 == am[0]); 2 does not (11); 3 agrees below 1 (20 == am[1]);
+    # 4 does not (99); 5 hangs below 2, which is not agreed; 6 does not (41 vs
+    # am[3] = 40); 7 agrees below 3 (40) -> path 0-1-3-7 of depth 3, bonus am[7]
+    assert oracle.lmhead.tree_accept_ref(tokens, parents, am) == (3, 7)
+    # a second node at the same depth with a lower index wins the tie
+    tokens_tie = [10, 11, 20, 99, 30, 40, 40]
+    assert oracle.lmhead.tree_accept_ref(tokens_tie, parents, am) == (3, 6)
+    # nothing agrees: only the root, depth 0, bonus am[0]
+    assert oracle.lmhead.tree_accept_ref([1, 2, 3, 4, 5, 6, 7], parents, am) == (0, 0)
+
+
+def test_tree_accept_invalid_parent_never_agrees():
+    am = [5, 6, 7, 8]
+    # node 2 names itself, node 3 a later node, as parent: neither can agree
+    assert oracle.lmhead.tree_accept_ref([5, 6, 7], [0, 2, 3], am) == (1, 1)
+    assert oracle.lmhead.tree_accept_ref([5, 5, 5], [-1, 0, 0], am) == (1, 2)
+    # node 2 below the later node 3 (which agrees below the root) still fails
+    assert oracle.lmhead.tree_accept_ref([5, 7, 5], [0, 3, 0], [5, 6, 7, 7]) == (1, 1)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(0, 2**31 - 1))
+def test_tree_accept_chain_is_greedy_accept(seed):
+    rng = np.random.default_rng(seed)
+    t = int(rng.integers(1, 18))
+    am = rng.integers(0, 4, size=t)
+    d = rng.integers(0, 4, size=t - 1)
+    depth, node = oracle.lmhead.tree_accept_ref(d, np.arange(t - 1), am)
+    assert depth == node == oracle.accept_len_ref(d, am)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(0, 2**31 - 1))
+def test_tree_accept_matches_forward_propagation(seed):
+    rng = np.random.default_rng(seed)
+    t = int(rng.integers(1, 24))
+    am = rng.integers(0, 3, size=t)
+    tokens = rng.integers(0, 3, size=t - 1)
+    parents = np.array([rng.integers(-1, i + 1) for i in range(1, t)], dtype=np.int64)
+    assert oracle.lmhead.tree_accept_ref(tokens, parents, am) == _agreed_forward(tokens, parents, am)
+
+
+def test_star_tree_takes_lowest_agreeing_child():
+    am = [3, 9, 9, 9, 9]
+    assert oracle.lmhead.tree_accept_ref([1, 3, 2, 3], [0, 0, 0, 0], am) == (1, 2)
+
+
+def test_lmhead_token_map_and_tree():
+    rng = np.random.default_rng(21)
+    m, v, k, t = 6, 40, 64, 6
+    wq, ws = synth.gen_weights(rng, v, k)
+    x = synth.gen_x(rng, m, k)
+    base = oracle.lmhead_ref(x, wq, ws, 1.0, T=1)
+    ident = oracle.lmhead_ref(x, wq, ws, 1.0, T=1, token_map=np.arange(v))
+    assert np.array_equal(base["argmax"], ident["argmax"])
+    perm = rng.permutation(v) + 1000
+    mapped = oracle.lmhead_ref(x, wq, ws, 1.0, T=1, token_map=perm)
+    assert np.array_equal(mapped["argmax_row"], base["argmax"])
+    assert np.array_equal(mapped["argmax"], perm[base["argmax"]])
+    # a chain given as parents gives the greedy result; a tree uses the rule
+    am = mapped["argmax"]
+    drafts = am[:t - 1].copy().reshape(1, t - 1)
+    drafts[0, 3] += 1
+    chain = oracle.lmhead_ref(x, wq, ws, 1.0, T=t, drafts=drafts, token_map=perm,
+                              parents=np.arange(t - 1).reshape(1, t - 1))
+    greedy = oracle.lmhead_ref(x, wq, ws, 1.0, T=t, drafts=drafts, token_map=perm)
+    assert chain["accept_len"][0] == greedy["accept_len"][0] == 3
+    star = np.zeros((1, t - 1), dtype=np.int64)
+    tree = oracle.lmhead_ref(x, wq, ws, 1.0, T=t, drafts=np.full((1, t - 1), am[0]), token_map=perm,
+                             parents=star)
+    assert tree["accept_len"][0] == 1 and tree["accept_node"][0] == 1

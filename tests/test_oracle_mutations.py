@@ -172,3 +172,72 @@ def test_planted_accept_off_by_one_is_caught(monkeypatch):
     am = np.arange(100, 117)
     assert bad(am[:16], am) != 16       # the constructed pin would fail
     assert oracle.accept_len_ref(am[:16], am) == 16
+
+
+# ---- tree accept: plausible wrong rules must fail the tree pins ------------
+
+def tree_pins_pass(fn) -> bool:
+    """The hand-worked tree, the tie rule, the invalid-parent rule and the
+    chain reduction, evaluated on a candidate tree-accept function."""
+    am = [10, 20, 30, 40, 50, 60, 70, 80]
+    parents = [0, 0, 1, 1, 2, 3, 3]
+    if fn([10, 11, 20, 99, 30, 41, 40], parents, am) != (3, 7):
+        return False
+    if fn([10, 11, 20, 99, 30, 40, 40], parents, am) != (3, 6):
+        return False
+    if fn([5, 6, 7], [0, 2, 3], [5, 6, 7, 8]) != (1, 1):
+        return False
+    # node 2 hangs below the later node 3, whose own path agrees
+    if fn([5, 7, 5], [0, 3, 0], [5, 6, 7, 7]) != (1, 1):
+        return False
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        t = int(rng.integers(2, 12))
+        a = rng.integers(0, 3, size=t)
+        d = rng.integers(0, 3, size=t - 1)
+        if fn(d, np.arange(t - 1), a)[0] != olm.accept_len_ref(d, a):
+            return False
+    return True
+
+
+def _walk_tree(rule):
+    """A tree accept built like the oracle's but with `rule(c, p, tokens,
+    argmax, parents)` deciding whether the step c -> p agrees, and ties
+    going by `tie`."""
+    def fn(tokens, parents, argmax, tie_high=False, count_nodes=False):
+        tokens, parents, argmax = (np.asarray(v).reshape(-1) for v in (tokens, parents, argmax))
+        best = (0, 0)
+        for i in range(1, argmax.shape[0]):
+            depth, c, ok = 0, i, True
+            while c != 0 and depth <= argmax.shape[0]:   # bounded: a mutant may follow a cycle
+                p = int(parents[c - 1])
+                if not rule(c, p, tokens, argmax):
+                    ok = False
+                    break
+                depth += 1
+                c = p
+            depth += 1 if (count_nodes and ok) else 0
+            if ok and (depth > best[0] or (tie_high and depth == best[0] and depth > 0)):
+                best = (depth, i)
+        return best
+    return fn
+
+
+def test_tree_pins_pass_for_the_oracle():
+    assert tree_pins_pass(olm.tree_accept_ref)
+
+
+@pytest.mark.parametrize("mutant", ["child_argmax", "no_parent_check", "tie_high", "count_nodes"])
+def test_planted_tree_mistake_is_caught(mutant):
+    good = lambda c, p, t, a: 0 <= p < c and int(t[c - 1]) == int(a[p])
+    if mutant == "child_argmax":      # compares with the child's own row
+        fn = _walk_tree(lambda c, p, t, a: 0 <= p < c and int(t[c - 1]) == int(a[c]))
+    elif mutant == "no_parent_check":  # follows parents that do not precede the child
+        fn = _walk_tree(lambda c, p, t, a: -1 < p < len(a) and p != c and int(t[c - 1]) == int(a[p]))
+    elif mutant == "tie_high":
+        base = _walk_tree(good)
+        fn = lambda t, p, a: base(t, p, a, tie_high=True)
+    else:
+        base = _walk_tree(good)
+        fn = lambda t, p, a: base(t, p, a, count_nodes=True)
+    assert not tree_pins_pass(fn)
