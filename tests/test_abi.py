@@ -16,7 +16,7 @@ from verify_gemm_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 VG_OK, VG_ERR_NULL, VG_ERR_SHAPE, VG_ERR_UNSUPPORTED = 0, -1, -2, -3
-VG_ERR_HIP, VG_ERR_WORKSPACE, VG_ERR_ALIGN = -4, -5, -6
+VG_ERR_HIP, VG_ERR_WORKSPACE, VG_ERR_ALIGN, VG_ERR_FLAGS = -4, -5, -6, -7
 
 
 @pytest.fixture(scope="module")
@@ -168,3 +168,30 @@ def test_binding_fails_loudly_without_library(tmp_path):
             binding.load(str(tmp_path / "missing.so"))
     finally:
         binding._lib = saved
+
+
+def test_invariant_and_verify_validation(lib, buf):
+    """The batch-invariant GEMM, lmhead_verify and vg_pass_create_ex validate
+    like their plain forms, and reject unknown flag bits."""
+    _, p = buf
+    assert lib.nvfp4_gemm_invariant(None, p, p, 1.0, 1, 16, 16, p, None) == VG_ERR_NULL
+    assert lib.nvfp4_gemm_invariant(p, p, p, 1.0, 1, 16, 24, p, None) == VG_ERR_SHAPE
+    assert lib.nvfp4_gemm_invariant(p, p, p, 1.0, 69, 16, 16, p, None) == VG_ERR_UNSUPPORTED
+    assert lib.nvfp4_gemm_invariant(p + 2, p, p, 1.0, 1, 16, 16, p, None) == VG_ERR_ALIGN
+    f = lib.lmhead_verify
+    ws = lib.vg_lmhead_workspace_bytes(17)
+    # X, Wq, Ws, g, tokens, parents, map, M, K, V, T, flags, argmax, len, node, ws, bytes, stream
+    assert f(p, p, p, 1.0, p, p, p, 17, 5120, 100, 17, 2, p, p, p, p, ws, None) == VG_ERR_FLAGS
+    assert f(p, p, p, 1.0, p, None, None, 17, 5120, 100, 17, 0, p, p, None, None, ws, None) == VG_ERR_WORKSPACE
+    assert f(p, p, p, 1.0, None, p, p, 17, 5120, 100, 17, 0, p, p, p, p, ws, None) == VG_ERR_NULL
+    assert f(p, p, p, 1.0, p, p, p, 17, 5120, 100, 5, 0, p, p, p, p, ws, None) == VG_ERR_SHAPE
+    assert f(p, p, p, 1.0, p, p, p, 17, 5120, 100, 17, 0, None, p, p, p, ws, None) == VG_ERR_NULL
+    out = ctypes.c_void_p()
+    J = binding.GemmJob
+    arr = (J * 1)(J(p, p, 1.0, 64, 128, p, p, 0))
+    assert lib.vg_pass_create_ex(ctypes.cast(arr, ctypes.c_void_p), 1, 1, None, None, None, None, 4,
+                                 ctypes.byref(out)) == VG_ERR_FLAGS
+    assert lib.vg_pass_create_ex(ctypes.cast(arr, ctypes.c_void_p), 1, 0, None, None, None, None, 1,
+                                 ctypes.byref(out)) == VG_ERR_SHAPE
+    assert out.value is None
+    assert lib.vg_status_string(VG_ERR_FLAGS).decode() == "unknown flag bits"

@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "vgemm.h")
 VG_OK = 0
 VG_MAX_M = 68
 VG_LMHEAD_K = 5120
+VG_BATCH_INVARIANT = 1
 
 _lib = None
 
@@ -58,6 +59,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "vg_pass_check": (i32, [vp, ctypes.POINTER(i32)]),
         "vg_pass_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "vg_pass_destroy": (None, [vp]),
+        "nvfp4_gemm_invariant": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp]),
+        "lmhead_verify": (i32, [vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                sz, vp]),
+        "vg_pass_create_ex": (i32, [vp, i32, i32, vp, vp, vp, vp, i32, ctypes.POINTER(vp)]),
         "vg_bwprobe": (i32, [vp, sz, vp, vp]),
         "vg_bwprobe_sink_floats": (sz, []),
         "vg_status_string": (ctypes.c_char_p, [i32]),
@@ -142,11 +147,12 @@ def new_workspace(nbytes: int, device=None):
     return torch.zeros(nbytes, dtype=torch.uint8, device=device or "cuda")
 
 
-def nvfp4_gemm(x, wq, ws, gscale: float, y=None, *, workspace=None, stream=None):
+def nvfp4_gemm(x, wq, ws, gscale: float, y=None, *, workspace=None, invariant=False, stream=None):
     """Y[M][N] = gscale * X . dequant(Wq, Ws)^T (fp32).  x: bf16 [M][K];
     wq: uint8 [N][K/2]; ws: uint8 [N][K/16].  With ``workspace`` (a zeroed
     uint8 device tensor of gemm_workspace_bytes bytes) the _ex entry point
-    is used, otherwise the library-owned workspace."""
+    is used, otherwise the library-owned workspace.  ``invariant`` selects
+    nvfp4_gemm_invariant (rows bit-identical for any M)."""
     torch = _torch()
     lib = load()
     px = _need(x, torch.bfloat16, 2, "X")
@@ -158,7 +164,9 @@ def nvfp4_gemm(x, wq, ws, gscale: float, y=None, *, workspace=None, stream=None)
     if tuple(y.shape) != (m, n):
         raise ValueError("Y must be [M][N]")
     sp = _stream_ptr(stream)
-    if workspace is None:
+    if invariant:
+        st = lib.nvfp4_gemm_invariant(px, wq.data_ptr(), ws.data_ptr(), float(gscale), m, n, k, py, sp)
+    elif workspace is None:
         st = lib.nvfp4_gemm(px, wq.data_ptr(), ws.data_ptr(), float(gscale), m, n, k, py, sp)
     else:
         pw = _need(workspace, torch.uint8, 1, "workspace")
@@ -217,6 +225,45 @@ def lmhead_argmax_accept_ex(x, wq, ws, gscale: float, draft_ids, T: int, workspa
     return argmax, accept_len
 
 
+def lmhead_verify(x, wq, ws, gscale: float, tokens, T: int, workspace, *, parents=None, token_map=None,
+                  flags: int = 0, argmax=None, accept_len=None, accept_node=None, stream=None):
+    """lmhead_verify: S = M/T trees (or chains, parents None) of T nodes;
+    tokens and parents int32 [S][T-1] (tokens None iff T == 1); token_map
+    int32 [V] or None; flags 0 or VG_BATCH_INVARIANT.  Returns (argmax,
+    accept_len, accept_node)."""
+    torch = _torch()
+    lib = load()
+    px = _need(x, torch.bfloat16, 2, "X")
+    m, k = x.shape
+    v = _check_weights(wq, ws, k)
+    s = m // T if T > 0 else 0
+    pt = pp = pm = None
+    if tokens is not None:
+        pt = _need(tokens, torch.int32, 2, "tokens")
+        if tuple(tokens.shape) != (s, T - 1):
+            raise ValueError("tokens must be [M/T][T-1]")
+    if parents is not None:
+        pp = _need(parents, torch.int32, 2, "parents")
+        if tuple(parents.shape) != (s, T - 1):
+            raise ValueError("parents must be [M/T][T-1]")
+    if token_map is not None:
+        pm = _need(token_map, torch.int32, 1, "token_map")
+        if token_map.numel() != v:
+            raise ValueError("token_map must have V entries")
+    dev = x.device
+    argmax = argmax if argmax is not None else torch.empty(m, dtype=torch.int32, device=dev)
+    accept_len = accept_len if accept_len is not None else torch.empty(max(s, 1), dtype=torch.int32, device=dev)
+    accept_node = accept_node if accept_node is not None else torch.empty(max(s, 1), dtype=torch.int32, device=dev)
+    pa = _need(argmax, torch.int32, 1, "argmax")
+    pl = _need(accept_len, torch.int32, 1, "accept_len")
+    pn = _need(accept_node, torch.int32, 1, "accept_node")
+    pw = _need(workspace, torch.uint8, 1, "workspace")
+    st = lib.lmhead_verify(px, wq.data_ptr(), ws.data_ptr(), float(gscale), pt, pp, pm, m, k, v, T,
+                           int(flags), pa, pl, pn, pw, workspace.numel(), _stream_ptr(stream))
+    _check(st, "lmhead_verify")
+    return argmax, accept_len, accept_node
+
+
 class GemmJob(ctypes.Structure):
     """vg_gemm_job of include/vgemm.h."""
     _fields_ = [("Wq", ctypes.c_void_p), ("Ws", ctypes.c_void_p), ("gscale", ctypes.c_float),
@@ -236,10 +283,13 @@ class Pass:
     """A whole step (vg_pass_*): GEMM jobs in dependency order plus an
     optional lm_head job, run as one persistent launch.  ``gemms`` is a list
     of (x, wq, ws, gscale, y, stage) with torch device tensors; ``lmhead`` is
-    (x, wq, ws, gscale, T, drafts, argmax, accept_len) or None.  The tensors
-    must outlive the Pass (it keeps references)."""
+    (x, wq, ws, gscale, T, drafts, argmax, accept_len) or None.  ``parents``,
+    ``token_map``, ``accept_node`` and ``flags`` are the lm_head options of
+    lmhead_verify (vg_pass_create_ex).  The tensors must outlive the Pass
+    (it keeps references)."""
 
-    def __init__(self, gemms, M: int, lmhead=None):
+    def __init__(self, gemms, M: int, lmhead=None, *, parents=None, token_map=None, accept_node=None,
+                 flags: int = 0):
         torch = _torch()
         lib = load()
         self._keep = []
@@ -268,10 +318,15 @@ class Pass:
             lm = LmheadJob(wq.data_ptr(), ws.data_ptr(), float(g), v, k, x.data_ptr(), int(T), pd,
                            am.data_ptr(), al.data_ptr())
             self._keep += [x, wq, ws, drafts, am, al]
+        pp = _need(parents, torch.int32, 2, "parents") if parents is not None else None
+        pm = _need(token_map, torch.int32, 1, "token_map") if token_map is not None else None
+        pn = _need(accept_node, torch.int32, 1, "accept_node") if accept_node is not None else None
+        self._keep += [parents, token_map, accept_node]
         h = ctypes.c_void_p()
-        st = lib.vg_pass_create(ctypes.cast(arr, ctypes.c_void_p), len(gemms), int(M),
-                                ctypes.byref(lm) if lm is not None else None, ctypes.byref(h))
-        _check(st, "vg_pass_create")
+        st = lib.vg_pass_create_ex(ctypes.cast(arr, ctypes.c_void_p), len(gemms), int(M),
+                                   ctypes.byref(lm) if lm is not None else None, pp, pm, pn, int(flags),
+                                   ctypes.byref(h))
+        _check(st, "vg_pass_create_ex")
         self._lib = lib
         self.handle = h
 

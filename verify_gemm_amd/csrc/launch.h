@@ -65,23 +65,29 @@ struct StreamArgs {
   int M;                         // rows of every X
   int T;                         // lm_head rows per sequence
   int has_lmhead;
-  const int32_t* drafts;         // [M/T][T-1]
+  const int32_t* drafts;         // [M/T][T-1]: tokens of nodes 1..T-1 of each sequence
   int32_t* argmax;               // [M]
   int32_t* accept_len;           // [M/T]
+  const int32_t* parents;        // [M/T][T-1] parent of nodes 1..T-1 (a tree), or null (a chain)
+  const int32_t* token_map;      // [V] token id of each lm_head row, or null (row index = id)
+  int32_t* accept_node;          // [M/T] node whose argmax is the bonus token, or null
+  int lm_rows;                   // V of the lm_head job (bounds the token_map lookup)
+  int invariant;                 // 1: every M on the MFMA path (row results independent of M)
 };
 
 enum StreamMode { STREAM_DIRECT = 0, STREAM_GRID = 1, STREAM_STATIC = 2 };
 
-// 0 for the M = 1 path, else the number of 16-row M-tiles.
-int stream_mt_class(int M);
+// 0 for the M = 1 GEMV path, else the number of 16-row M-tiles.  A batch-
+// invariant launch never takes the GEMV path (M = 1 runs as one M-tile).
+int stream_mt_class(int M, bool invariant);
 // Weight rows per item for a batch of M rows and a reduction length K.
-int stream_rows_per_item(int M, int K);
+int stream_rows_per_item(int M, int K, bool invariant);
 // DIRECT: grid = items of a.job0.  GRID: a.job0 walked by up to `grid`
 // resident workgroups.  STATIC: the job list of a step, items assigned
 // round-robin to a grid of co-resident workgroups (at most `grid`).
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream);
 // The exact grid a STATIC launch of a batch of M rows uses (all resident).
-int stream_static_grid(int M);
+int stream_static_grid(int M, bool invariant);
 
 // M = 1: the whole step (or a single GEMM / lm_head) as one launch of
 // step_gemv_grid() resident workgroups; rows of every job split evenly.

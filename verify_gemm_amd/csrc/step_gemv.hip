@@ -66,10 +66,10 @@
 // deadlock.
 //
 // lm_head: compute waves keep their best (logit, lowest index) and publish
-// it once at the end; the last workgroup out writes argmax, runs the greedy
-// accept rule (TandemLLM README, introduction; with one row there are no
-// drafts, so accept_len = 0) and zeroes the control block for the next
-// launch.
+// it once at the end; the last workgroup out writes argmax (as a token id
+// through the head's row map when there is one), runs the accept rule
+// (TandemLLM README, introduction; with one row there are no drafts, so
+// accept_len = 0) and zeroes the control block for the next launch.
 #include <type_traits>
 
 #include "launch.h"
@@ -755,8 +755,11 @@ __global__ __launch_bounds__(kWG) void step_gemv_kernel(StreamArgs a) {
         best = k > best ? k : best;
         __hip_atomic_store(&ctl->keys[0][s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      a.argmax[0] = (int)key_index(best);
+      // one row (T = 1): no drafts, so only the root is agreed
+      const int row = (int)key_index(best);
+      a.argmax[0] = a.token_map && row >= 0 && row < a.lm_rows ? a.token_map[row] : row;
       a.accept_len[0] = 0;
+      if (a.accept_node) a.accept_node[0] = 0;
     }
     st_agent(&ctl->exits, 0u);
   }

@@ -563,8 +563,20 @@ __device__ void signal_stage(const StreamArgs& a, int s) {
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The last workgroup out: argmax from the key slots, greedy accept, reset.
-__device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am) {
+// The last workgroup out: argmax from the key slots (reported as token ids
+// through the head's row map when there is one), the accept rule, reset.
+//
+// Accept (TandemLLM README, flow diagram and "The parts": the drafters'
+// guesses form a tree and the target keeps the longest path it agrees
+// with): node 0 of a sequence is the committed position; node i >= 1 holds
+// drafts[i-1] below parent parents[i-1], or below i-1 when there is no
+// parent array (a chain).  Node i is agreed iff its parent p lies in
+// [0, i), p is agreed and drafts[i-1] equals the argmax of row p.  Parents
+// precede their children, so one pass in node order settles every node.
+// The deepest agreed node (lowest index among equals) gives accept_len
+// (its depth) and accept_node; for a chain that is the longest agreeing
+// prefix.  Parents outside [0, i) are never followed.
+__device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am, int* lds_dep) {
   const int tid = threadIdx.x;
   if (a.has_lmhead) {
     for (int m = tid; m < a.M; m += kWG) {
@@ -575,17 +587,31 @@ __device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am) 
         best = k > best ? k : best;
         __hip_atomic_store(&ctl->keys[m][s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      const int am = (int)key_index(best);
+      const int row = (int)key_index(best);
+      const int am = a.token_map && row >= 0 && row < a.lm_rows ? a.token_map[row] : row;
       lds_am[m] = am;
       a.argmax[m] = am;
     }
     __syncthreads();
     const int S = a.M / a.T;
     for (int q = tid; q < S; q += kWG) {
-      int L = 0;
       const int32_t* d = a.drafts + (size_t)q * (a.T - 1);
-      while (L < a.T - 1 && d[L] == lds_am[q * a.T + L]) ++L;
-      a.accept_len[q] = L;
+      const int32_t* par = a.parents ? a.parents + (size_t)q * (a.T - 1) : nullptr;
+      const int* am = lds_am + q * a.T;
+      int* dep = lds_dep + q * a.T;  // depth of an agreed node, -1 otherwise
+      dep[0] = 0;
+      int best_d = 0, best_n = 0;
+      for (int i = 1; i < a.T; ++i) {
+        const int p = par ? par[i - 1] : i - 1;
+        const bool ok = p >= 0 && p < i && dep[p] >= 0 && d[i - 1] == am[p];
+        dep[i] = ok ? dep[p] + 1 : -1;
+        if (ok && dep[i] > best_d) {
+          best_d = dep[i];
+          best_n = i;
+        }
+      }
+      a.accept_len[q] = best_d;
+      if (a.accept_node) a.accept_node[q] = best_n;
     }
   }
   if (a.waits)
@@ -601,6 +627,7 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
   __shared__ float red[kRed];
   __shared__ int lds_flag;
   __shared__ int lds_am[VG_MAX_M_DEV];
+  __shared__ int lds_dep[VG_MAX_M_DEV];
   Best<MT == 0 ? 1 : MT * 4> best;
   best.init();
 
@@ -662,7 +689,7 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
     __syncthreads();
     if (!lds_flag) return;
     __threadfence();
-    finish_lmhead(ctl, a, lds_am);
+    finish_lmhead(ctl, a, lds_am, lds_dep);
   }
 }
 
@@ -710,10 +737,10 @@ hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream
 
 }  // namespace
 
-int stream_mt_class(int M) { return M == 1 ? 0 : (M + 15) / 16; }
+int stream_mt_class(int M, bool invariant) { return M == 1 && !invariant ? 0 : (M + 15) / 16; }
 
-int stream_rows_per_item(int M, int K) {
-  const int mt = stream_mt_class(M);
+int stream_rows_per_item(int M, int K, bool invariant) {
+  const int mt = stream_mt_class(M, invariant);
   if (mt == 0) {
     if (K == 5120) return GemvItem<5, 4>::kRows;
     if (K == 17408) return GemvItem<17, 1>::kRows;
@@ -723,12 +750,12 @@ int stream_rows_per_item(int M, int K) {
   return 16 * (mt <= 2 ? 2 : 4);
 }
 
-int stream_static_grid(int M) {
+int stream_static_grid(int M, bool invariant) {
   // All workgroups must be resident (the static schedule waits on them);
   // one per CU measured best: more only park more prefetched items behind
   // the stage waits.
   int cap = 0;
-  switch (stream_mt_class(M)) {
+  switch (stream_mt_class(M, invariant)) {
     case 0: cap = resident_blocks<0, MODE_STATIC>(); break;
     case 1: cap = resident_blocks<1, MODE_STATIC>(); break;
     case 2: cap = resident_blocks<2, MODE_STATIC>(); break;
@@ -740,7 +767,7 @@ int stream_static_grid(int M) {
 }
 
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
-  switch (stream_mt_class(a.M)) {
+  switch (stream_mt_class(a.M, a.invariant != 0)) {
     case 0: return launch_mt<0>(a, mode, grid, stream);
     case 1: return launch_mt<1>(a, mode, grid, stream);
     case 2: return launch_mt<2>(a, mode, grid, stream);
