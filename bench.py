@@ -3,15 +3,21 @@
 One step = one pass over the whole hot path: 64 layers x {q, k, v, o, gate,
 up, down} NVFP4 GEMMs + the lm_head with fused argmax and greedy accept
 (449 matrices, 14,115,962,880 weight bytes), run as ONE persistent kernel
-launch of the native step executor (vg_pass_run).  Reported at M = 1 (plain
+launch of the native step executor (vg_pass_run).  Each layer's q, k, v (and
+gate, up) are stored back to back and read as one stacked matrix -- 257 jobs
+-- with each member's own tensor scale kept as per-row scales, so every
+output has the same bits as with 449 separate jobs (the fused projections
+of dgx-spark-qwen38 README, opening section).  Reported at M = 1 (plain
 decode), 4, 17 (16 drafts + 1) and 68 (4 sequences x 17): microseconds per
 pass and effective weight GB/s against the 8 TB/s HBM peak.  ``value`` is
 the M = 1 figure; every batch size is in ``per_m``.
 
 Also measured in the same run:
   * the read ceiling of a pure streaming-read kernel (vg_bwprobe);
-  * the same step as one launch per matrix, captured in a HIP graph
-    (``unfused_graph_us_per_pass``): the schedule the single launch replaces;
+  * the same step as one launch per job, captured in a HIP graph
+    (``unfused_graph_us_per_pass``), and as 449 separate jobs, one launch
+    and one launch per job (``separate_jobs``): the schedules the single
+    launch replaces;
   * ``roofline``: the dominant kernel is the step kernel itself (the whole
     pass is one launch): 14,115,962,880 weight bytes per launch over its
     event-timed average duration at the first M;
@@ -155,7 +161,11 @@ def main():
     ms_list = [int(v) for v in args.ms.split(",")]
     per_m = {}
     for M in ms_list:
-        run = weightpass.PassRun(weights, M)
+        # The timed step: every layer's {q,k,v} and {gate,up} read as one
+        # stacked matrix each (257 jobs), each member keeping its own tensor
+        # scale as per-row scales -- the same bytes and the same output bits
+        # as 449 separate jobs -- in one persistent launch.
+        run = weightpass.PassRun(weights, M, fused=True)
         run.run()
         torch.cuda.synchronize()
         if run.check():
@@ -166,12 +176,26 @@ def main():
         gbps = wbytes / (ms * 1e-3) / 1e9
         entry = {"us_per_pass": round(ms * 1000, 2), "weight_gbps": round(gbps, 1),
                  "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-                 "pct_of_probe": round(100 * gbps / probe, 2)}
+                 "pct_of_probe": round(100 * gbps / probe, 2), "jobs": run.step.info()["jobs"]}
         if not args.no_unfused:
+            reps = max(2, min(args.steps, 5))
             g = run.capture_unfused()
-            so = time_launches(g.replay, max(2, min(args.steps, 5)), 1)
-            entry["unfused_graph_us_per_pass"] = round(so * 1000, 1)
+            entry["unfused_graph_us_per_pass"] = round(time_launches(g.replay, reps, 1) * 1000, 1)
             del g
+            # the same step as 449 separate jobs, as one launch and as one
+            # launch per job
+            sr = weightpass.PassRun(weights, M)
+            sr.run()
+            torch.cuda.synchronize()
+            if sr.check():
+                raise RuntimeError(f"M={M}: a stage wait timed out in the 449-job step")
+            sep = time_launches(sr.run, reps, 1)
+            gs = sr.capture_unfused()
+            entry["separate_jobs"] = {"jobs": sr.step.info()["jobs"], "us_per_pass": round(sep * 1000, 2),
+                                      "unfused_graph_us_per_pass": round(time_launches(gs.replay, reps, 1) * 1000, 1)}
+            del gs
+            sr.close()
+            del sr
         per_m[str(M)] = entry
         log(f"[bench] M={M}: {entry}")
         run.close()
@@ -195,7 +219,9 @@ def main():
         "data": "synthetic (seeded device RNG, codes uniform, scales 2^u)",
         "config": {"workload": "full synthetic weight pass: 64 layers x {q,k,v,o 5120x5120; gate,up "
                                "17408x5120; down 5120x17408} + lm_head 248320x5120 with argmax/accept "
-                               f"(449 NVFP4 matrices, {wbytes} weight bytes), one persistent launch per pass",
+                               f"(449 NVFP4 matrices, {wbytes} weight bytes), one persistent launch per pass; "
+                               "each layer's q|k|v and gate|up read as one stacked matrix (257 jobs, per-matrix "
+                               "tensor scales kept as per-row scales, outputs bit-identical to 449 jobs)",
                    "M": ms_list[0], "M_reported": ms_list},
         "per_m": per_m,
         "bwprobe_read_gbps": round(probe, 1),

@@ -81,3 +81,54 @@ def test_full_step_lmhead_argmax_accept(weights):
     print(f"full-step lm_head: decisive rows {int(dec.sum())}/17, accept_len {al} "
           f"(oracle {int(ref['accept_len'][0])})", flush=True)
     run.close()
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
+@pytest.mark.parametrize("M", [1, 17])
+def test_fused_projections_full_size(weights, M):
+    """{q, k, v} and {gate, up} as one job each (257 jobs, each member's
+    tensor scale kept as per-row scales): the same bits as the separate
+    jobs, in the one-launch and the one-launch-per-job schedules; sampled
+    fused outputs against the oracle."""
+    print(f"[case] fused projections M={M}", flush=True)
+    sep = weightpass.PassRun(weights, M)
+    fus = weightpass.PassRun(weights, M, fused=True)
+    assert fus.step.info()["jobs"] == 4 * weights.layers + 1
+    sep.run()
+    fus.run()
+    torch.cuda.synchronize()
+    assert sep.check() == 0 and fus.check() == 0
+    for layer in range(weights.layers):
+        s = sep.y[7 * layer:7 * layer + 7]
+        f = fus.y[4 * layer:4 * layer + 4]
+        assert torch.equal(_bits(f[0]), _bits(torch.cat(s[0:3], 1))), f"layer {layer} qkv"
+        assert torch.equal(_bits(f[1]), _bits(s[3])), f"layer {layer} o"
+        assert torch.equal(_bits(f[2]), _bits(torch.cat(s[4:6], 1))), f"layer {layer} gate|up"
+        assert torch.equal(_bits(f[3]), _bits(s[6])), f"layer {layer} down"
+    assert torch.equal(sep.argmax, fus.argmax) and torch.equal(sep.accept_len, fus.accept_len)
+    rng = np.random.default_rng(43000 + M)
+    xs = {k: host_bits(v) for k, v in fus.x.items()}
+    for layer, gname, yi in [(0, "qkv", 0), (63, "gateup", 4 * 63 + 2)]:
+        grp = weights.fused[layer][gname]
+        members = [m for m in weights.mats if m["layer"] == layer and m["name"] in grp["members"]]
+        y = fus.y[yi].cpu().numpy()
+        r0 = 0
+        for mem in members:   # each member's rows with its own tensor scale
+            rows = rng.integers(0, mem["n"], 16)
+            ms = rng.integers(0, M, 16)
+            idx = torch.from_numpy(rows).cuda()
+            wq, ws = mem["wq"][idx].cpu().numpy(), mem["ws"][idx].cpu().numpy()
+            pairs = list(zip(ms.tolist(), rows.tolist()))
+            ye, be = oracle.nvfp4_gemm_ref_entries(xs[grp["k"]], wq, ws, mem["g"], pairs)
+            got = np.array([y[a, r0 + b] for a, b in pairs], dtype=np.float64)
+            assert np.all(np.abs(got - ye) <= be), f"fused {gname} of layer {layer}, {mem['name']}"
+            r0 += mem["n"]
+    first = [y.clone() for y in fus.y]
+    fus.run_unfused()
+    torch.cuda.synchronize()
+    assert all(torch.equal(_bits(a), _bits(b)) for a, b in zip(first, fus.y))
+    sep.close()
+    fus.close()

@@ -205,3 +205,34 @@ def test_pass_batch_invariant_rows_and_tree():
     assert int(lm1[0].cpu()[0]) == int(am[0])
     p1.close()
     p17.close()
+
+
+@pytest.mark.parametrize("M", [1, 4, 17])
+def test_row_scales_stack_matrices_bitwise(M):
+    """Two matrices stacked by rows as one job with per-row scales (each
+    member's own tensor scale) give the same bits as two jobs, in the
+    one-launch and one-launch-per-job schedules; K = 5120 (step kernel at
+    M = 1) and K = 48 (the stream kernel's generic path).  304 rows keep the
+    second member's code and scale rows 16-byte aligned at both K."""
+    print(f"[case] row scales M={M}", flush=True)
+    rng = np.random.default_rng(44000 + M)
+    for k in (5120, 48):
+        parts = [synth.gen_weights(rng, n, k) for n in (304, 208)]
+        gs = [synth.gen_gscale(rng), synth.gen_gscale(rng)]
+        x = dev_bf16(synth.gen_x(rng, M, k))
+        wq = dev_u8(np.concatenate([p[0] for p in parts]))
+        ws = dev_u8(np.concatenate([p[1] for p in parts]))
+        rs = torch.cat([torch.full((304,), gs[0]), torch.full((208,), gs[1])]).float().cuda()
+        ya = torch.empty((M, 304), device="cuda")
+        yb = torch.empty((M, 208), device="cuda")
+        yf = torch.empty((M, 512), device="cuda")
+        sep = binding.Pass([(x, wq[:304], ws[:304], gs[0], ya, 0), (x, wq[304:], ws[304:], gs[1], yb, 0)], M)
+        fus = binding.Pass([(x, wq, ws, 123.0, yf, 0, rs)], M)   # gscale ignored with row scales
+        for run in ("run", "run_unfused"):
+            yf.fill_(float("nan"))
+            getattr(sep, run)()
+            getattr(fus, run)()
+            torch.cuda.synchronize()
+            assert same_bits(yf, torch.cat([ya, yb], 1)), f"K={k} {run}"
+        sep.close()
+        fus.close()

@@ -268,7 +268,7 @@ class GemmJob(ctypes.Structure):
     """vg_gemm_job of include/vgemm.h."""
     _fields_ = [("Wq", ctypes.c_void_p), ("Ws", ctypes.c_void_p), ("gscale", ctypes.c_float),
                 ("N", ctypes.c_int), ("K", ctypes.c_int), ("X", ctypes.c_void_p),
-                ("Y", ctypes.c_void_p), ("stage", ctypes.c_int)]
+                ("Y", ctypes.c_void_p), ("stage", ctypes.c_int), ("row_scale", ctypes.c_void_p)]
 
 
 class LmheadJob(ctypes.Structure):
@@ -282,7 +282,8 @@ class LmheadJob(ctypes.Structure):
 class Pass:
     """A whole step (vg_pass_*): GEMM jobs in dependency order plus an
     optional lm_head job, run as one persistent launch.  ``gemms`` is a list
-    of (x, wq, ws, gscale, y, stage) with torch device tensors; ``lmhead`` is
+    of (x, wq, ws, gscale, y, stage[, row_scale]) with torch device tensors
+    (row_scale: float32 [N] or None, see vg_gemm_job); ``lmhead`` is
     (x, wq, ws, gscale, T, drafts, argmax, accept_len) or None.  ``parents``,
     ``token_map``, ``accept_node`` and ``flags`` are the lm_head options of
     lmhead_verify (vg_pass_create_ex).  The tensors must outlive the Pass
@@ -294,16 +295,23 @@ class Pass:
         lib = load()
         self._keep = []
         arr = (GemmJob * max(len(gemms), 1))()
-        for i, (x, wq, ws, g, y, stage) in enumerate(gemms):
+        for i, job in enumerate(gemms):
+            x, wq, ws, g, y, stage = job[:6]
+            rs = job[6] if len(job) > 6 else None
             _need(x, torch.bfloat16, 2, "X")
             _need(y, torch.float32, 2, "Y")
             k = x.shape[1]
             n = _check_weights(wq, ws, k)
             if tuple(y.shape) != (M, n) or x.shape[0] != M:
                 raise ValueError("X must be [M][K] and Y [M][N]")
+            prs = None
+            if rs is not None:
+                prs = _need(rs, torch.float32, 1, "row_scale")
+                if rs.numel() != n:
+                    raise ValueError("row_scale must have N entries")
             arr[i] = GemmJob(wq.data_ptr(), ws.data_ptr(), float(g), n, k, x.data_ptr(), y.data_ptr(),
-                             int(stage))
-            self._keep += [x, wq, ws, y]
+                             int(stage), prs)
+            self._keep += [x, wq, ws, y, rs]
         lm = None
         if lmhead is not None:
             x, wq, ws, g, T, drafts, am, al = lmhead

@@ -21,6 +21,7 @@ struct StreamJob {
   const uint8_t* ws;  // [n][k/16]
   const uint16_t* x;  // [M][k] bf16 bits
   float* y;           // [M][n] (kind 0)
+  const float* gr;    // [n] per-row output scale (kind 0; then g == 1), or null
   float g;
   int n;
   int k;
@@ -28,7 +29,7 @@ struct StreamJob {
   int item_begin;
   int items;
   int kind;           // 0: GEMM, 1: lm_head (argmax, no output matrix)
-  int pad;
+  int pad[3];         // to a multiple of 16 bytes (the job table is copied in 16-byte pieces)
 };
 
 // Device-side control block of a launch that has an lm_head (argmax keys)

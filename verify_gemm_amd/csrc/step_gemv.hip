@@ -600,12 +600,15 @@ __device__ void prepare(const StreamArgs& a, Shared& sh, const StreamJob& j, IoS
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
-// Stores the results of chunk ch (LDS area `parity`) and clears that
-// area's completion count for the chunk after next.
-__device__ void flush(Shared& sh, const StreamJob& j, const Chunk& ch, int parity) {
+// Stores the results of chunk ch (LDS area `parity`; lane t owns row t)
+// times this lane's row scale `rsc`, and clears that area's completion
+// count for the chunk after next.  With per-row scales the job's g is 1
+// and the sum is exact so far, so sum * rsc is the one rounding sum * g
+// would be; without them rsc == 1 (exact).
+static_assert(kMaxChunkRows <= kWave, "one store lane per chunk row");
+__device__ void flush(Shared& sh, const StreamJob& j, const Chunk& ch, int parity, float rsc) {
   const int lane = threadIdx.x & 63;
-  if (j.kind == 0)
-    for (int t = lane; t < ch.rows; t += kWave) store_out(&j.y[ch.r0 + t], sh.res[parity][t]);
+  if (j.kind == 0 && lane < ch.rows) store_out(&j.y[ch.r0 + lane], sh.res[parity][lane] * rsc);
   if (lane == 0) lds_store(&sh.done[parity], 0u);
 }
 
@@ -681,8 +684,12 @@ __device__ __forceinline__ void store_loop(const StreamArgs& a, Shared& sh, int 
   for (;;) {
     const bool more = next_chunk(sh, njobs, cu, nxt);
     const StreamJob j = lds_job(sh, cur.job);
+    // the chunk's row scales are read before its results are awaited, so
+    // that read is not between "results ready" and the stores
+    const int lane = threadIdx.x & 63;
+    const float rsc = j.kind == 0 && j.gr && lane < cur.rows ? j.gr[cur.r0 + lane] : 1.0f;
     wait_done(a, sh, parity);
-    flush(sh, j, cur, parity);
+    flush(sh, j, cur, parity, rsc);
     // the LDS reads of the flush have completed before the areas are handed back
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if ((threadIdx.x & 63) == 0) lds_store(&sh.flushed, k + 1);

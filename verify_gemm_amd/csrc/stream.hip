@@ -73,6 +73,15 @@ __device__ __forceinline__ void store_out(float* p, float v) {
   __hip_atomic_store((VG_GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The output scale of row n of a GEMM job with per-row scales (g == 1
+// there, so the row sum is exact up to the store, and sum * scale is the
+// same single rounding as sum * g of a job with one scale); 1 otherwise.
+// Read right after the item's weight loads are issued, so the value has
+// long arrived when the result is stored.
+__device__ __forceinline__ float row_scale(const StreamJob& j, int n) {
+  return j.kind == 0 && j.gr && n < j.n ? j.gr[n] : 1.0f;
+}
+
 // Thread 0 polls until `target` workgroups have signalled stage `s`.
 __device__ bool wait_stage(StageCounter (*sd)[kDoneSlots], StreamCtl* ctl, int s, unsigned target) {
   for (long it = 0; it < kSpinLimit; ++it) {
@@ -433,6 +442,9 @@ template <int CPL, int RH, class Dep, class BestT>
 __device__ __forceinline__ void gemv_run(const StreamJob& j, int item, Dep&& dep, BestT& best) {
   GemvItem<CPL, RH> it;
   it.issue(j, item);
+  float rsc[RH];
+#pragma unroll
+  for (int i = 0; i < RH; ++i) rsc[i] = row_scale(j, it.row(i));
   const bool ok = dep();
   float acc[RH];
   it.compute(j, acc);
@@ -442,7 +454,7 @@ __device__ __forceinline__ void gemv_run(const StreamJob& j, int item, Dep&& dep
 #pragma unroll
       for (int i = 0; i < RH; ++i) {
         const int r = it.row(i);
-        if (r < j.n) store_out(&j.y[r], acc[i]);
+        if (r < j.n) store_out(&j.y[r], acc[i] * rsc[i]);
       }
     }
   } else {
@@ -458,11 +470,12 @@ template <class Dep, class BestT>
 __device__ __forceinline__ void gemv_generic_run(const StreamJob& j, int item, Dep&& dep, BestT& best) {
   GemvGenericItem it;
   it.issue(j, item);
+  const float rsc = row_scale(j, it.r);
   const bool ok = dep();
   const float v = it.compute(j);
   if (!ok || it.r >= j.n) return;
   if (j.kind == 0) {
-    if ((threadIdx.x & 63) == 0) store_out(&j.y[it.r], v);
+    if ((threadIdx.x & 63) == 0) store_out(&j.y[it.r], v * rsc);
   } else {
     best.offer(0, v, it.r);
   }
@@ -472,6 +485,9 @@ template <int MT, int NT, class Item, class Dep, class BestT>
 __device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item, int M, Dep&& dep,
                                          float* red, BestT& best) {
   it.issue(j, item);
+  float rsc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rsc[nt] = row_scale(j, it.n0 + 16 * nt + (threadIdx.x & 15));
   const bool ok = dep();
   it.compute(j, M);
   reduce_waves<MT, NT>(it.acc, red, j.g);
@@ -487,7 +503,7 @@ __device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item,
         for (int nt = 0; nt < NT; ++nt) {
           const int n = it.n0 + 16 * nt + c;
           if (n < j.n) {
-            if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], it.acc[mt][nt][r]);
+            if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], it.acc[mt][nt][r] * rsc[nt]);
             else best.offer(mt * 4 + r, it.acc[mt][nt][r], n);
           }
         }
