@@ -12,8 +12,10 @@ Contents
 ``nvfp4``   closed-form E2M1 / E4M3 / bf16 decoding, nibble unpacking,
             dequantisation and the fp64 GEMM with its acceptance bound.
 ``lmhead``  the lm_head pass: per-row argmax (lowest index on ties),
-            top-2 gap against the bound (near-tie classification) and the
-            greedy accept-prefix length.
+            top-2 gap against the bound (near-tie classification), the
+            greedy accept-prefix length, tree verify and the sliced head's
+            row-to-token map.
+``fp8``     FP8 (E4M3) weights with tensor and per-row scales.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values that
 do not come from the oracle itself (exact rational brute force, library
@@ -32,6 +34,7 @@ from .nvfp4 import (  # noqa: F401
     unpack_codes,
     tolerance_bound,
 )
+from .fp8 import fp8_dequant, fp8_gemm_ref  # noqa: F401
 from .lmhead import (  # noqa: F401
     accept_len_ref,
     lmhead_ref,

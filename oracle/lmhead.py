@@ -47,6 +47,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import fp8_dequant
 from .nvfp4 import bf16_bits_to_f64, dequant, tolerance_bound
 
 
@@ -151,20 +152,22 @@ def _compared_rows(tokens, parents, argmax) -> list[int]:
     return sorted(rows)
 
 
-def _row_bound(ax_row: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float, v: int) -> float:
+def _row_bound(ax_row: np.ndarray, deq, v: int) -> float:
     """Acceptance bound of logit (row, v): one dot product of |x| and |w_v|."""
-    w = dequant(wq[v:v + 1], ws[v:v + 1], g)[0]
+    w = deq(v, v + 1)[0]
     return float(tolerance_bound(np.dot(ax_row, np.abs(w))))
 
 
 def lmhead_ref(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float,
                T: int, drafts: np.ndarray | None = None, *,
                token_map: np.ndarray | None = None, parents: np.ndarray | None = None,
-               interval: bool = False, row_chunk: int = 4096) -> dict:
+               fp8: bool = False, interval: bool = False, row_chunk: int = 4096) -> dict:
     """Run the lm_head verify pass on the CPU.
 
     x_bits uint16[M][K] (bf16 bits), wq uint8[V][K/2], ws uint8[V][K/16],
-    g the tensor scale (part of every logit).  M must be a multiple of T;
+    g the tensor scale (part of every logit).  With ``fp8`` the head is FP8
+    (``oracle.fp8``): wq is uint8[V][K] E4M3 bytes and ws the per-row
+    scales float[V] or None.  M must be a multiple of T;
     drafts int[M/T][T-1] or None (then no accept lengths are computed).
     token_map int[V] or None: head row r stands for token token_map[r]
     (``argmax`` then holds token ids, ``argmax_row`` the rows).  parents
@@ -184,17 +187,26 @@ def lmhead_ref(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float,
     if T < 1 or m % T:
         raise ValueError("M must be a positive multiple of T")
     wq = np.asarray(wq, dtype=np.uint8)
-    ws = np.asarray(ws, dtype=np.uint8)
+    if fp8:
+        rs = None if ws is None else np.asarray(ws, dtype=np.float32)
+
+        def deq(r0, r1):
+            return fp8_dequant(wq[r0:r1], None if rs is None else rs[r0:r1], g)
+    else:
+        ws = np.asarray(ws, dtype=np.uint8)
+
+        def deq(r0, r1):
+            return dequant(wq[r0:r1], ws[r0:r1], g)
     nv = wq.shape[0]
     v1 = np.full(m, -np.inf); i1 = np.full(m, -1, dtype=np.int64)
     v2 = np.full(m, -np.inf); i2 = np.full(m, -1, dtype=np.int64)
     for r0 in range(0, nv, row_chunk):
         r1 = min(nv, r0 + row_chunk)
-        logits = x @ dequant(wq[r0:r1], ws[r0:r1], g).T
+        logits = x @ deq(r0, r1).T
         v1, i1, v2, i2 = top2_merge(v1, i1, v2, i2, *_chunk_top2(logits, r0))
     ax = np.abs(x)
-    b1 = np.array([_row_bound(ax[r], wq, ws, g, int(i1[r])) for r in range(m)])
-    b2 = np.array([_row_bound(ax[r], wq, ws, g, int(i2[r])) if i2[r] >= 0 else 0.0
+    b1 = np.array([_row_bound(ax[r], deq, int(i1[r])) for r in range(m)])
+    b2 = np.array([_row_bound(ax[r], deq, int(i2[r])) if i2[r] >= 0 else 0.0
                    for r in range(m)])
     ids = i1 if token_map is None else np.asarray(token_map, dtype=np.int64)[i1]
     out = {
@@ -209,7 +221,7 @@ def lmhead_ref(x_bits: np.ndarray, wq: np.ndarray, ws: np.ndarray, g: float,
         rows = np.arange(m)
         for r0 in range(0, nv, row_chunk):
             r1 = min(nv, r0 + row_chunk)
-            w = dequant(wq[r0:r1], ws[r0:r1], g)
+            w = deq(r0, r1)
             hi = x @ w.T + tolerance_bound(ax @ np.abs(w).T)
             inside = (i1 >= r0) & (i1 < r1)
             hi[rows[inside], i1[inside] - r0] = -np.inf
