@@ -195,3 +195,19 @@ def test_invariant_and_verify_validation(lib, buf):
                                  ctypes.byref(out)) == VG_ERR_SHAPE
     assert out.value is None
     assert lib.vg_status_string(VG_ERR_FLAGS).decode() == "unknown flag bits"
+
+
+def test_fp8_validation(lib, buf):
+    _, p = buf
+    assert lib.fp8_gemm(None, p, None, 1.0, 1, 16, 16, p, None) == VG_ERR_NULL
+    assert lib.fp8_gemm(p, None, None, 1.0, 1, 16, 16, p, None) == VG_ERR_NULL
+    assert lib.fp8_gemm(p, p, None, 1.0, 1, 16, 24, p, None) == VG_ERR_SHAPE
+    assert lib.fp8_gemm(p, p, None, 1.0, 69, 16, 16, p, None) == VG_ERR_UNSUPPORTED
+    assert lib.fp8_gemm(p, p + 8, None, 1.0, 1, 16, 16, p, None) == VG_ERR_ALIGN
+    assert lib.fp8_gemm(p, p, p + 2, 1.0, 1, 16, 16, p, None) == VG_ERR_ALIGN      # row scales
+    f = lib.lmhead_verify_fp8
+    ws = lib.vg_lmhead_workspace_bytes(17)
+    assert f(p, p, None, 1.0, p, None, None, 17, 5120, 100, 17, 4, p, p, None, p, ws, None) == VG_ERR_FLAGS
+    assert f(p, p, None, 1.0, None, None, None, 17, 5120, 100, 17, 0, p, p, None, p, ws, None) == VG_ERR_NULL
+    assert f(p, p, p + 1, 1.0, p, None, None, 17, 5120, 100, 17, 0, p, p, None, p, ws, None) == VG_ERR_ALIGN
+    assert f(p, p, None, 1.0, p, None, None, 17, 5120, 100, 17, 0, p, p, None, None, ws, None) == VG_ERR_WORKSPACE

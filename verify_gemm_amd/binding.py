@@ -63,6 +63,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lmhead_verify": (i32, [vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                 sz, vp]),
         "vg_pass_create_ex": (i32, [vp, i32, i32, vp, vp, vp, vp, i32, ctypes.POINTER(vp)]),
+        "fp8_gemm": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp]),
+        "lmhead_verify_fp8": (i32, [vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                    sz, vp]),
         "vg_bwprobe": (i32, [vp, sz, vp, vp]),
         "vg_bwprobe_sink_floats": (sz, []),
         "vg_status_string": (ctypes.c_char_p, [i32]),
@@ -261,6 +264,60 @@ def lmhead_verify(x, wq, ws, gscale: float, tokens, T: int, workspace, *, parent
     st = lib.lmhead_verify(px, wq.data_ptr(), ws.data_ptr(), float(gscale), pt, pp, pm, m, k, v, T,
                            int(flags), pa, pl, pn, pw, workspace.numel(), _stream_ptr(stream))
     _check(st, "lmhead_verify")
+    return argmax, accept_len, accept_node
+
+
+def fp8_gemm(x, w8, gscale: float, row_scale=None, y=None, *, stream=None):
+    """Y[M][N] = X . W^T, w = gscale * row_scale[n] * E4M3(w8): x bf16 [M][K],
+    w8 uint8 [N][K], row_scale float32 [N] or None."""
+    torch = _torch()
+    lib = load()
+    px = _need(x, torch.bfloat16, 2, "X")
+    m, k = x.shape
+    pw = _need(w8, torch.uint8, 2, "W8")
+    n = w8.shape[0]
+    if w8.shape[1] != k:
+        raise ValueError("W8 must be [N][K]")
+    pr = None
+    if row_scale is not None:
+        pr = _need(row_scale, torch.float32, 1, "row_scale")
+        if row_scale.numel() != n:
+            raise ValueError("row_scale must have N entries")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    py = _need(y, torch.float32, 2, "Y")
+    if tuple(y.shape) != (m, n):
+        raise ValueError("Y must be [M][N]")
+    _check(lib.fp8_gemm(px, pw, pr, float(gscale), m, n, k, py, _stream_ptr(stream)), "fp8_gemm")
+    return y
+
+
+def lmhead_verify_fp8(x, w8, gscale: float, tokens, T: int, workspace, *, row_scale=None, parents=None,
+                      token_map=None, flags: int = 0, stream=None):
+    """lmhead_verify with an FP8 head (w8 uint8 [V][K], row_scale float32 [V]
+    or None).  Returns (argmax, accept_len, accept_node)."""
+    torch = _torch()
+    lib = load()
+    px = _need(x, torch.bfloat16, 2, "X")
+    m, k = x.shape
+    pw = _need(w8, torch.uint8, 2, "W8")
+    v = w8.shape[0]
+    if w8.shape[1] != k:
+        raise ValueError("W8 must be [V][K]")
+    s = m // T if T > 0 else 0
+    pt = _need(tokens, torch.int32, 2, "tokens") if tokens is not None else None
+    pp = _need(parents, torch.int32, 2, "parents") if parents is not None else None
+    pm = _need(token_map, torch.int32, 1, "token_map") if token_map is not None else None
+    pr = _need(row_scale, torch.float32, 1, "row_scale") if row_scale is not None else None
+    dev = x.device
+    argmax = torch.empty(m, dtype=torch.int32, device=dev)
+    accept_len = torch.empty(max(s, 1), dtype=torch.int32, device=dev)
+    accept_node = torch.empty(max(s, 1), dtype=torch.int32, device=dev)
+    pws = _need(workspace, torch.uint8, 1, "workspace")
+    st = lib.lmhead_verify_fp8(px, pw, pr, float(gscale), pt, pp, pm, m, k, v, T, int(flags),
+                               argmax.data_ptr(), accept_len.data_ptr(), accept_node.data_ptr(), pws,
+                               workspace.numel(), _stream_ptr(stream))
+    _check(st, "lmhead_verify_fp8")
     return argmax, accept_len, accept_node
 
 

@@ -29,7 +29,8 @@ struct StreamJob {
   int item_begin;
   int items;
   int kind;           // 0: GEMM, 1: lm_head (argmax, no output matrix)
-  int pad[3];         // to a multiple of 16 bytes (the job table is copied in 16-byte pieces)
+  int fmt;            // weight format: 0 NVFP4 (wq codes, ws block scales), 1 FP8 E4M3 (wq [n][k] bytes)
+  int pad[2];         // to a multiple of 16 bytes (the job table is copied in 16-byte pieces)
 };
 
 // Device-side control block of a launch that has an lm_head (argmax keys)
@@ -82,7 +83,7 @@ enum StreamMode { STREAM_DIRECT = 0, STREAM_GRID = 1, STREAM_STATIC = 2 };
 // invariant launch never takes the GEMV path (M = 1 runs as one M-tile).
 int stream_mt_class(int M, bool invariant);
 // Weight rows per item for a batch of M rows and a reduction length K.
-int stream_rows_per_item(int M, int K, bool invariant);
+int stream_rows_per_item(int M, int K, bool invariant, int fmt);
 // DIRECT: grid = items of a.job0.  GRID: a.job0 walked by up to `grid`
 // resident workgroups.  STATIC: the job list of a step, items assigned
 // round-robin to a grid of co-resident workgroups (at most `grid`).

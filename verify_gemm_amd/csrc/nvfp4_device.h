@@ -106,6 +106,31 @@ __device__ __forceinline__ float dot8(unsigned w, u32x4 x, float acc) {
   return acc;
 }
 
+// FP8 (E4M3) weights: bytes 2*hi and 2*hi+1 of a dword -> two bf16, exact
+// (E4M3 values have 4 significant bits and exponents within bf16's range).
+template <bool hi>
+__device__ __forceinline__ bf16x2 e4m3x2_bf16(unsigned w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, hi);
+}
+// Eight E4M3 weights (two dwords, element order = byte order) dotted with
+// eight bf16 activations (one 16-byte piece), accumulated onto acc.
+__device__ __forceinline__ float fp8_dot8(unsigned w0, unsigned w1, u32x4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_bf16<false>(w0), as_bf16x2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_bf16<true>(w0), as_bf16x2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_bf16<false>(w1), as_bf16x2(x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_bf16<true>(w1), as_bf16x2(x.w), acc, false);
+  return acc;
+}
+// Eight E4M3 weights as the bf16x8 operand of a bf16 MFMA.
+__device__ __forceinline__ bf16x8 fp8x8_bf16(unsigned w0, unsigned w1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(unsigned, e4m3x2_bf16<false>(w0));
+  r[1] = __builtin_bit_cast(unsigned, e4m3x2_bf16<true>(w0));
+  r[2] = __builtin_bit_cast(unsigned, e4m3x2_bf16<false>(w1));
+  r[3] = __builtin_bit_cast(unsigned, e4m3x2_bf16<true>(w1));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // One 16-element block: codes (2 dwords), x (4 dwords-of-pairs x 2), scale.
 __device__ __forceinline__ float block16(unsigned c0, unsigned c1, u32x4 xa, u32x4 xb, float s,
                                          float acc) {

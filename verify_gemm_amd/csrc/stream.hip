@@ -73,13 +73,15 @@ __device__ __forceinline__ void store_out(float* p, float v) {
   __hip_atomic_store((VG_GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The output scale of row n of a GEMM job with per-row scales (g == 1
-// there, so the row sum is exact up to the store, and sum * scale is the
-// same single rounding as sum * g of a job with one scale); 1 otherwise.
-// Read right after the item's weight loads are issued, so the value has
-// long arrived when the result is stored.
+// The scale of output row n of a job with per-row scales, 1 otherwise.  A
+// GEMM job that stacks matrices keeps each member's tensor scale this way
+// (its g is 1, so the row sum is exact up to the store, and sum * scale is
+// the same single rounding as sum * g of a job with one scale); an FP8
+// job's per-row scales multiply its outputs, or its logits before the
+// argmax.  Read right after the item's weight loads are issued, so the
+// value has long arrived when the result is used.
 __device__ __forceinline__ float row_scale(const StreamJob& j, int n) {
-  return j.kind == 0 && j.gr && n < j.n ? j.gr[n] : 1.0f;
+  return j.gr && n < j.n ? j.gr[n] : 1.0f;
 }
 
 // Thread 0 polls until `target` workgroups have signalled stage `s`.
@@ -357,6 +359,94 @@ struct MfmaGuardedItem {
   }
 };
 
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) weights: one byte per element, W8[N][K]; g and the per-row
+// scales multiply a row's sum.  E4M3 converts to bf16 exactly, so the
+// arithmetic is that of the NVFP4 items: v_dot2 at M = 1, bf16 MFMA at
+// M >= 2.  Any K % 16 == 0 (a 16-byte piece is 16 elements, a multiple of
+// the 8 the MFMA steps take, so a piece is all in or all out of K).
+// ---------------------------------------------------------------------------
+// M = 1: each wave owns one row of a 4-row item; lane L takes the 16-byte
+// pieces L, L+64, ... of the row (1 KB per wave instruction), four pieces
+// in flight.
+struct Fp8GemvItem {
+  static constexpr int kRows = kWaves;
+  int r;
+  __device__ __forceinline__ void issue(const StreamJob& j, int item) {
+    r = item * kRows + (threadIdx.x >> 6);
+  }
+  __device__ __forceinline__ float compute(const StreamJob& j) {
+    const int lane = threadIdx.x & 63;
+    const int rr = r < j.n ? r : j.n - 1;
+    const int np = j.k >> 4;
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(j.wq + (size_t)rr * j.k);
+    const u32x4* xp = reinterpret_cast<const u32x4*>(j.x);
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 4
+    for (int p = lane; p < np; p += kWave) {
+      const u32x4 w = ld_stream(wrow + p);
+      a0 = fp8_dot8(w[0], w[1], ld_act(xp + 2 * p), a0);
+      a1 = fp8_dot8(w[2], w[3], ld_act(xp + 2 * p + 1), a1);
+    }
+    return sum_lanes<64>(a0 + a1) * j.g;
+  }
+};
+
+// M >= 2: as MfmaGuardedItem -- the four waves split the 128-element
+// windows, lane (c, gq) holds K positions win*128 + 32*gq + 8*st + 0..7 of
+// row n0 + 16*nt + c (weights) and of activation row 16*mt + c.
+template <int MT, int NT>
+struct Fp8MfmaItem {
+  static constexpr int kRows = 16 * NT;
+  f32x4 acc[MT][NT];
+  int n0;
+  __device__ __forceinline__ void issue(const StreamJob&, int item) { n0 = item * kRows; }
+  __device__ __forceinline__ void compute(const StreamJob& j, int M) {
+    const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4, w = threadIdx.x >> 6;
+    const uint8_t* wrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      int n = n0 + 16 * nt + c;
+      n = n < j.n ? n : j.n - 1;
+      wrow[nt] = j.wq + (size_t)n * (size_t)j.k;
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nw = (j.k + 127) >> 7;
+    const int wb = (w * nw) / kWaves, we = ((w + 1) * nw) / kWaves;
+    for (int win = wb; win < we; ++win) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int e0 = win * 128 + 32 * gq + 8 * st;
+        const bool ok = e0 < j.k;
+        bf16x8 b[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          unsigned w0 = 0, w1 = 0;
+          if (ok) {
+            const unsigned* p = reinterpret_cast<const unsigned*>(wrow[nt] + e0);
+            w0 = ld_stream(p);
+            w1 = ld_stream(p + 1);
+          }
+          b[nt] = fp8x8_bf16(w0, w1);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = 16 * mt + c;
+          u32x4 a = {0u, 0u, 0u, 0u};
+          if (ok && m < M) a = ld_act(reinterpret_cast<const u32x4*>(j.x + (size_t)m * j.k + e0));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b[nt],
+                                                                  acc[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+};
+
 // The four waves' partial tiles meet in LDS and are added in wave order
 // 0+1+2+3 by wave 0, which then owns the finished tile (times g).
 template <int MT, int NT>
@@ -461,14 +551,15 @@ __device__ __forceinline__ void gemv_run(const StreamJob& j, int item, Dep&& dep
 #pragma unroll
     for (int i = 0; i < RH; ++i) {
       const int r = it.row(i);
-      if (r < j.n) best.offer(0, acc[i], r);
+      if (r < j.n) best.offer(0, acc[i] * rsc[i], r);
     }
   }
 }
 
-template <class Dep, class BestT>
+// One row per wave (GemvGenericItem: NVFP4, any K; Fp8GemvItem: FP8).
+template <class Item, class Dep, class BestT>
 __device__ __forceinline__ void gemv_generic_run(const StreamJob& j, int item, Dep&& dep, BestT& best) {
-  GemvGenericItem it;
+  Item it;
   it.issue(j, item);
   const float rsc = row_scale(j, it.r);
   const bool ok = dep();
@@ -477,7 +568,7 @@ __device__ __forceinline__ void gemv_generic_run(const StreamJob& j, int item, D
   if (j.kind == 0) {
     if ((threadIdx.x & 63) == 0) store_out(&j.y[it.r], v * rsc);
   } else {
-    best.offer(0, v, it.r);
+    best.offer(0, v * rsc, it.r);
   }
 }
 
@@ -504,7 +595,7 @@ __device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item,
           const int n = it.n0 + 16 * nt + c;
           if (n < j.n) {
             if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], it.acc[mt][nt][r] * rsc[nt]);
-            else best.offer(mt * 4 + r, it.acc[mt][nt][r], n);
+            else best.offer(mt * 4 + r, it.acc[mt][nt][r] * rsc[nt], n);
           }
         }
       }
@@ -515,13 +606,17 @@ template <int MT, class Dep, class BestT>
 __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, Dep&& dep, float* red,
                                          BestT& best) {
   if constexpr (MT == 0) {
-    if (j.k == 5120) gemv_run<5, 4>(j, item, dep, best);
+    if (j.fmt == 1) gemv_generic_run<Fp8GemvItem>(j, item, dep, best);
+    else if (j.k == 5120) gemv_run<5, 4>(j, item, dep, best);
     else if (j.k == 17408) gemv_run<17, 1>(j, item, dep, best);
     else if (j.k == 1024) gemv_run<1, 8>(j, item, dep, best);
-    else gemv_generic_run(j, item, dep, best);
+    else gemv_generic_run<GemvGenericItem>(j, item, dep, best);
   } else {
     constexpr int NT = Cfg<MT>::NT;
-    if ((j.k & 127) == 0) {
+    if (j.fmt == 1) {
+      Fp8MfmaItem<MT, NT> it;
+      mfma_run<MT, NT>(it, j, item, M, dep, red, best);
+    } else if ((j.k & 127) == 0) {
       MfmaItem<MT, NT, Cfg<MT>::P, Cfg<MT>::XPF> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
     } else {
@@ -755,8 +850,9 @@ hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream
 
 int stream_mt_class(int M, bool invariant) { return M == 1 && !invariant ? 0 : (M + 15) / 16; }
 
-int stream_rows_per_item(int M, int K, bool invariant) {
+int stream_rows_per_item(int M, int K, bool invariant, int fmt) {
   const int mt = stream_mt_class(M, invariant);
+  if (mt == 0 && fmt == 1) return Fp8GemvItem::kRows;
   if (mt == 0) {
     if (K == 5120) return GemvItem<5, 4>::kRows;
     if (K == 17408) return GemvItem<17, 1>::kRows;

@@ -60,6 +60,16 @@ def gen_weights(rng: np.random.Generator, n: int, k: int):
     return wq, ws
 
 
+def gen_fp8_weights(rng: np.random.Generator, n: int, k: int, row_scales: bool = True):
+    """FP8 weights: E4M3 bytes uint8[n][k] uniform over the 254 non-NaN
+    codes (so every exponent, subnormals and +-448 included), and per-row
+    scales float32[n] ~ U[0.5, 2] (None if not row_scales)."""
+    w8 = rng.integers(0, 254, size=(n, k), dtype=np.uint16)
+    w8 = (w8 + (w8 >= 0x7F)).astype(np.uint8)       # skip 0x7F; 254 -> 0xFF never drawn
+    rs = rng.uniform(0.5, 2.0, size=n).astype(np.float32) if row_scales else None
+    return w8, rs
+
+
 def gen_scale_bytes(rng: np.random.Generator, n: int, k: int, codes: np.ndarray):
     """Block-scale bytes drawn uniformly from an explicit set of byte codes."""
     codes = np.asarray(codes, dtype=np.uint8)
