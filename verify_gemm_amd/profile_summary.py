@@ -70,12 +70,20 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
         f.write("\n".join(lines))
 
 
+# The fill kernel of known size is one of many torch fills in a run (small
+# buffers are filled too): only its dispatches, the large ones, calibrate.
+CALIBRATION_FILL = "torch fill (write reference)"
+
+
 def _per_dispatch(path: str, counter: str):
     agg = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
         n = short_name(r["Kernel_Name"])
         if n is not None and r["Counter_Name"] == counter:
             agg[n].append(float(r["Counter_Value"]))
+    if CALIBRATION_FILL in agg:
+        top = max(agg[CALIBRATION_FILL])
+        agg[CALIBRATION_FILL] = [v for v in agg[CALIBRATION_FILL] if v >= 0.5 * top]
     return {k: sum(v) / len(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()}
 
 
@@ -84,7 +92,7 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
     fetch, nf = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write, nw = _per_dispatch(write_csv, "WRITE_SIZE")
     f_scale = probe_bytes / (fetch["bwprobe_kernel (read probe)"] * 1024)
-    w_scale = fill_bytes / (write["torch fill (write reference)"] * 1024)
+    w_scale = fill_bytes / (write[CALIBRATION_FILL] * 1024)
     traffic = {}
     for k in sorted(set(fetch) | set(write)):
         if k.startswith("step_gemv") or k.startswith("stream_kernel"):
@@ -97,7 +105,8 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
         lines.append(f"| {k} | {nf.get(k, 0)} | {fetch.get(k, 0):.6g} | {write.get(k, 0):.6g} |")
     lines += ["", f"Scale factors from the kernels of known size: reads x{f_scale:.4f} "
               f"(the probe reads {probe_bytes} bytes per dispatch), writes x{w_scale:.4f} "
-              f"(torch's fill writes {fill_bytes} bytes per dispatch).", "",
+              f"(torch's fill of the probe buffer writes {fill_bytes} bytes per dispatch; the "
+              "smaller fills of the same run are left out).", "",
               "Traffic per launch (scaled fetch + scaled write) against the pass's algorithmic "
               f"{PASS_WEIGHT_BYTES} weight bytes:", ""]
     for k, v in traffic.items():
