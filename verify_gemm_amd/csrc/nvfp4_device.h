@@ -112,6 +112,65 @@ template <bool hi>
 __device__ __forceinline__ bf16x2 e4m3x2_bf16(unsigned w) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, hi);
 }
+// A buffer descriptor over `bytes` bytes at `base` (raw, stride 0): loads
+// at offsets past `bytes` return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// rsrc for a base and range that are wave-uniform in fact but that the
+// compiler may not prove uniform: both go through readfirstlane, so the
+// descriptor lives in scalar registers (a descriptor in vector registers
+// makes the compiler wrap every load in a loop over its distinct values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_uniform(const void* base, unsigned bytes) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  // readfirstlane returns a signed int: widen through unsigned, or a low
+  // word with bit 31 set would sign-extend into the high word
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const unsigned long long u = ((unsigned long long)hi << 32) | (unsigned long long)lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// The same buffer descriptor as four scalar words, for dma16.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, unsigned bytes) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)b);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) & 0xFFFFu;  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// LDS address (byte offset) of a location in LDS.
+template <class T>
+__device__ __forceinline__ unsigned lds_addr(T* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) T*)p;
+}
+
+// One 1-KB global-to-LDS copy: lane i's 16 bytes at byte `voff` of buffer
+// `rs` land at LDS byte lds + 16 * i.  An offset past the buffer's range
+// reads nothing from memory, but the lane still writes its 16 LDS bytes,
+// so every lane's destination must lie inside the area being filled.
+// Written as assembly so that the compiler does not track it: it would
+// otherwise wait for every LDS copy in flight before any LDS read of this
+// wave (including the copies made ahead of time).  Completion is awaited
+// explicitly (vmcnt) by the caller.  The compiler emits no other LDS copy,
+// so it keeps nothing in M0 across this.  `lds` must be wave-uniform; it is
+// moved to a scalar register here (the "s" constraint alone does not make
+// the compiler move a value that lives in a vector register).
+__device__ __forceinline__ void dma16(u32x4 rs, unsigned voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m)
+               : "memory", "m0");
+}
+
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt bits 3:0
+// and 15:14; expcnt 7 and lgkmcnt 15 = no wait on those).
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) | 0x0F70u; }
+
 // Eight E4M3 weights (two dwords, element order = byte order) dotted with
 // eight bf16 activations (one 16-byte piece), accumulated onto acc.
 __device__ __forceinline__ float fp8_dot8(unsigned w0, unsigned w1, u32x4 x, float acc) {

@@ -133,42 +133,6 @@ __device__ __forceinline__ void lds_store(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-// The same buffer descriptor as four scalar words, for the DMA below.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, unsigned bytes) {
-  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((unsigned)b);
-  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32)) & 0xFFFFu;  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000u;
-  return r;
-}
-
-// LDS address (byte offset) of a location in LDS.
-template <class T>
-__device__ __forceinline__ unsigned lds_addr(T* p) {
-  return (unsigned)(size_t)(__attribute__((address_space(3))) T*)p;
-}
-
-// One 1-KB global-to-LDS copy: lane i's 16 bytes at byte `voff` of buffer
-// `rs` land at LDS byte lds + 16 * i; an offset past the buffer's range
-// reads nothing.  Written as assembly so that the compiler does not track
-// it: it would otherwise wait for every LDS copy in flight before any LDS
-// read of this wave (including the copies made ahead of time).  Completion
-// is awaited explicitly (vmcnt) by the I/O wave.  The compiler emits no
-// other LDS copy in this kernel, so it keeps nothing in M0 across this.
-// `lds` must be wave-uniform; it is moved to a scalar register here (the
-// "s" constraint alone does not make the compiler move a value that lives
-// in a vector register).
-__device__ __forceinline__ void dma16(u32x4 rs, unsigned voff, unsigned lds) {
-  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m)
-               : "memory", "m0");
-}
 
 __host__ __device__ __forceinline__ int pieces_per_lane(int k) { return (k + 1023) >> 10; }
 __host__ __device__ __forceinline__ int rows_per_half(int k) {

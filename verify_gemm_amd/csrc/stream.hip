@@ -56,6 +56,8 @@ namespace {
 constexpr int kWG = 256;
 constexpr int kWaves = kWG / kWave;
 constexpr long kSpinLimit = 1L << 23;  // ~0.2 s of polling before giving up
+constexpr unsigned kOOB = 0x80000000u;  // buffer offset past every range used here
+constexpr int kNT = 2;                  // buffer-load cache policy: nontemporal
 
 // ---------------------------------------------------------------------------
 // control block helpers
@@ -303,6 +305,162 @@ struct MfmaItem {
   }
 };
 
+// M >= 2, K % 128 == 0: activations shared through LDS.  The four waves
+// split the item's rows -- wave w owns the NT tiles of 16 rows n0 +
+// 16*(NT*w + nt) + c -- and walk K together, one 128-element window at a
+// time.  Every wave loads, P windows ahead, the weights of its own rows and
+// its quarter of the activation window (rows 4*MT*w .. 4*MT*(w+1) - 1 of
+// the 16*MT rows; lanes 16r..16r+15 read the 256 bytes of one row), both
+// into registers with ordinary loads the compiler tracks -- so its waits
+// are exact.  One window before use each wave writes its quarter into an
+// LDS double buffer; after a barrier all waves read the whole window from
+// there: the activations cross the memory path once per workgroup instead
+// of once per wave.  Rows past M load as zeros.
+//
+// LDS layout of a slot: activation row m at byte 256*m; its 16-byte piece
+// q (elements 8q..8q+7 of the window) at position q ^ (m & 15), so that
+// the 16 lanes reading rows 16*mt + c, piece q, hit 16 different bank
+// groups (and the 16 lanes writing one row hit 16 different ones too).
+// Lane (c, gq) of MFMA step st takes piece 4*gq + st of its row, the same
+// K positions as its weight code dword st.
+template <int MT, int NT, int P>
+struct MfmaLdsItem {
+  static constexpr int kRows = 16 * NT * kWaves;
+  static constexpr int kSlotBytes = 16 * MT * 256;
+  static constexpr int kRing = 2;  // slots: the window being read, the next one being written
+  u32x4 q[P][NT];
+  unsigned short sc[P][NT];
+  u32x4 xq[P][MT];  // this wave's quarter of the activation window, per ring position
+  f32x4 acc[MT][NT];
+  __amdgpu_buffer_rsrc_t rw[NT], rs[NT], rx;
+  unsigned cw, cs;  // this lane's code / scale byte offset within its tile
+  int n0, nwin;
+
+  // Weights are loaded with the default cache policy, not nontemporal: a
+  // window takes 64 bytes of each row's 128-byte line and the next window
+  // the other half, and with the streaming policy the line is often gone
+  // by then (measured: 1.12x the weight bytes fetched against 1.05x, and
+  // the 248,320-row lm_head at M = 17 28 % faster with the default).
+  __device__ __forceinline__ void load_w(int p, int v) {
+    const bool in = v < nwin;  // wave-uniform
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      q[p][nt] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? cw + 64u * (unsigned)v : kOOB, 0, 0);
+      sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b16(rs[nt], in ? cs + 8u * (unsigned)v : kOOB, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const StreamJob& j, int item) {
+    const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned rb = (unsigned)j.k >> 1, sb = (unsigned)j.k >> 4;
+    n0 = item * kRows;
+    nwin = j.k >> 7;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t0 = n0 + 16 * (NT * w + nt);
+      const int rows = j.n - t0 < 0 ? 0 : (j.n - t0 > 16 ? 16 : j.n - t0);
+      rw[nt] = rsrc_uniform(j.wq + (size_t)t0 * rb, (unsigned)rows * rb);
+      rs[nt] = rsrc_uniform(j.ws + (size_t)t0 * sb, (unsigned)rows * sb);
+    }
+    cw = (unsigned)c * rb + 16u * (unsigned)gq;
+    cs = (unsigned)c * sb + 2u * (unsigned)gq;
+#pragma unroll
+    for (int p = 0; p < P; ++p) load_w(p, p);
+  }
+
+  // Row of this lane's activation piece i (wave w's quarter).
+  __device__ __forceinline__ int xrow(int i) const {
+    return 4 * (MT * (int)(threadIdx.x >> 6) + i) + ((threadIdx.x & 63) >> 4);
+  }
+
+  __device__ __forceinline__ void load_x(int p, int v, int k) {
+    const unsigned piece = threadIdx.x & 15;
+    const bool in = v < nwin;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const unsigned off = (unsigned)xrow(i) * (unsigned)k * 2u + 256u * (unsigned)v + 16u * piece;
+      xq[p][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? off : kOOB, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void store_x(int p, unsigned char* slot) {
+    const unsigned piece = threadIdx.x & 15;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = xrow(i);
+      *reinterpret_cast<u32x4*>(slot + 256 * m + 16 * (piece ^ (unsigned)(m & 15))) = xq[p][i];
+    }
+  }
+
+  __device__ __forceinline__ void window(int p, const unsigned char* slot) {
+    const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 b[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const f32x2 s = e4m3x2_lo(sc[p][nt]);
+        b[nt] = dequant8_bf16(q[p][nt][st], st < 2 ? s[0] : s[1]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + c;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(slot + 256 * m + 16 * ((4 * gq + st) ^ c));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b[nt],
+                                                                acc[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // After the stage wait: the activations of the first P windows, then
+  // every window in order.  `lds` holds kRing slots of kSlotBytes.
+  __device__ __forceinline__ void compute(const StreamJob& j, int M, unsigned char* lds) {
+    rx = rsrc_uniform(j.x, (unsigned)M * (unsigned)j.k * 2u);
+#pragma unroll
+    for (int p = 0; p < P; ++p) load_x(p, p, j.k);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    store_x(0, lds);
+    // The loop over whole groups of P windows must be entered in the order
+    // its own iterations leave the loads in, and contain no skipped step:
+    // a loop header reached with another order (the first P windows' loads
+    // went out as all weights before the stage wait, then all activations)
+    // or with fewer loads (a skipped step) gets the compiler's most
+    // conservative wait -- all loads -- in every iteration.  So the first
+    // group is peeled off, the loop runs whole groups only, and the last,
+    // partial group (or all of a short K) is done step by step.
+    int base = 0;
+    if (nwin >= 2 * P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) step(p, p, j.k, lds);
+      for (base = P; base + P <= nwin; base += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) step(p, base + p, j.k, lds);
+      }
+    }
+    for (; base < nwin; base += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (base + p < nwin) step(p, base + p, j.k, lds);
+    }
+  }
+
+  // Window v (ring position p = v % P): compute it, pass the next window's
+  // activations to LDS, and load window v + P into position p.
+  __device__ __forceinline__ void step(int p, int v, int k, unsigned char* lds) {
+    __syncthreads();  // window v is in LDS; every wave is done with window v-1
+    window(p, lds + (v & 1) * kSlotBytes);
+    store_x(p + 1 < P ? p + 1 : 0, lds + ((v + 1) & 1) * kSlotBytes);
+    load_x(p, v + P, k);
+    load_w(p, v + P);
+  }
+};
+
 // Any K % 16 == 0, predicated everywhere: each wave takes a quarter of the
 // (possibly partial) 128-element windows.
 template <int MT, int NT>
@@ -523,6 +681,10 @@ struct Cfg {
   static constexpr int NT = MT <= 2 ? 2 : 4;   // weight rows per item: 32 or 64
   static constexpr int P = MT <= 2 ? 6 : 2;    // 128-element windows in flight per wave (even)
   static constexpr bool XPF = MT <= 2;         // prefetch the next window's activations
+  // the LDS-shared item (K % 128 == 0): 16-row tiles per wave, window ring depth
+  static constexpr int LNT = 1;
+  static constexpr int LP = MT <= 2 ? 6 : 4;
+  using Lds = MfmaLdsItem<MT, LNT, LP>;
 };
 
 // Processes one item of job j.  `dep` is called by every thread after the
@@ -602,9 +764,43 @@ __device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item,
     }
 }
 
+// The LDS-shared MFMA item: each wave finishes its own rows (no reduction).
+template <int MT, class Dep, class BestT>
+__device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M, Dep&& dep, unsigned char* xring,
+                                             BestT& best) {
+  using Item = typename Cfg<MT>::Lds;
+  constexpr int NT = Cfg<MT>::LNT;
+  const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4, w = threadIdx.x >> 6;
+  Item it;
+  it.issue(j, item);
+  float rsc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rsc[nt] = row_scale(j, it.n0 + 16 * (NT * w + nt) + c);
+  const bool ok = dep();
+  it.compute(j, M, xring);
+  if (!ok) return;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 16 * mt + 4 * gq + r;
+      if (m < M) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = it.n0 + 16 * (NT * w + nt) + c;
+          if (n < j.n) {
+            const float v = it.acc[mt][nt][r] * j.g * rsc[nt];
+            if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], v);
+            else best.offer(mt * 4 + r, v, n);
+          }
+        }
+      }
+    }
+}
+
 template <int MT, class Dep, class BestT>
 __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, Dep&& dep, float* red,
-                                         BestT& best) {
+                                         unsigned char* xring, BestT& best) {
   if constexpr (MT == 0) {
     if (j.fmt == 1) gemv_generic_run<Fp8GemvItem>(j, item, dep, best);
     else if (j.k == 5120) gemv_run<5, 4>(j, item, dep, best);
@@ -617,8 +813,7 @@ __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, De
       Fp8MfmaItem<MT, NT> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
     } else if ((j.k & 127) == 0) {
-      MfmaItem<MT, NT, Cfg<MT>::P, Cfg<MT>::XPF> it;
-      mfma_run<MT, NT>(it, j, item, M, dep, red, best);
+      mfma_lds_run<MT>(j, item, M, dep, xring, best);
     } else {
       MfmaGuardedItem<MT, NT> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
@@ -627,7 +822,8 @@ __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, De
 }
 
 // Publish the workgroup's lm_head bests (M = 1: every wave's best; M >= 2:
-// wave 0's per-lane bests reduced over the 16 lanes sharing rows).
+// every wave's per-lane bests reduced over the 16 lanes sharing rows --
+// waves that hold none publish nothing).
 template <int MT, class BestT>
 __device__ __forceinline__ void publish(StreamCtl* ctl, int M, BestT& best) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -639,7 +835,7 @@ __device__ __forceinline__ void publish(StreamCtl* ctl, int M, BestT& best) {
     if (oi >= 0 && (i < 0 || better(ov, oi, v, i))) { v = ov; i = oi; }
     if (lane == 0) publish_best(ctl, 0, v, i);
   } else {
-    if (w != 0) return;
+    (void)w;
     const int c = lane & 15, gq = lane >> 4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -736,6 +932,8 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
   constexpr int NT = MT == 0 ? 1 : Cfg<MT>::NT;
   constexpr int kRed = MT == 0 ? 1 : (kWaves - 1) * MT * NT * 4 * kWave;
   __shared__ float red[kRed];
+  constexpr int kXRing = MT == 0 ? 16 : Cfg<(MT > 0 ? MT : 1)>::Lds::kRing * Cfg<(MT > 0 ? MT : 1)>::Lds::kSlotBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char xring[kXRing];
   __shared__ int lds_flag;
   __shared__ int lds_am[VG_MAX_M_DEV];
   __shared__ int lds_dep[VG_MAX_M_DEV];
@@ -744,7 +942,7 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
 
   if constexpr (MODE == MODE_DIRECT) {
     auto nodep = [] { return true; };
-    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, best);
+    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, best);
     return;
   } else {
     StreamCtl* ctl = a.ctl;
@@ -784,8 +982,10 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
         }
         return true;
       };
-      run_item<MT>(j, item, a.M, dep, red, best);
-      if constexpr (MODE == MODE_STATIC) __syncthreads();  // LDS reuse by the next item
+      run_item<MT>(j, item, a.M, dep, red, xring, best);
+      // LDS reuse by the next item (M >= 2: its activation copies go into
+      // ring slots the slowest wave may still be reading)
+      if constexpr (MODE == MODE_STATIC || MT > 0) __syncthreads();
     }
     if constexpr (MODE == MODE_STATIC) {
       if (my_stage >= 0) signal_stage(a, my_stage);
@@ -859,6 +1059,7 @@ int stream_rows_per_item(int M, int K, bool invariant, int fmt) {
     if (K == 1024) return GemvItem<1, 8>::kRows;
     return GemvGenericItem::kRows;
   }
+  if (fmt == 0 && (K & 127) == 0) return Cfg<1>::Lds::kRows;  // the LDS-shared item (same rows for every MT)
   return 16 * (mt <= 2 ? 2 : 4);
 }
 
