@@ -114,6 +114,40 @@ def test_one_layer_step(M, T):
     p.close()
 
 
+SPREAD = [(1280, 17408, 0), (333, 5120, 1), (4096, 1024, 2)]
+
+
+@pytest.mark.parametrize("M", [2, 17, 68])
+def test_spread_slices(M):
+    """Narrow matrices at M >= 2 are dealt as K slices of 64-row blocks, one
+    item per slice, the slice sums added in slice order by the workgroup
+    that completes a block.  The item count shows which stages are spread
+    (1280 x 17408: 20 blocks x 3 slices; 333 x 5120: 6 x 3; 4096 x 1024:
+    one slice, 64 blocks; lm_head 1000 x 2048: 16 x 2); the bits equal the
+    one-launch-per-matrix schedule, where one workgroup runs every slice of
+    a block; repeated launches (the per-block counts reset themselves) give
+    the same bits; every output is within the oracle's bound."""
+    print(f"[case] spread slices M={M}", flush=True)
+    p, host, ys, lm, lmhost = build(M, 1, SPREAD, (1000, 2048), 33000 + M)
+    assert p.info()["items"] == 60 + 18 + 64 + 32
+    p.run()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    check_outputs(M, 1, host, ys, lm, lmhost, f"spread M={M}")
+    first = snapshot(ys, lm)
+    for _ in range(3):
+        p.run()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    assert same(first, snapshot(ys, lm))
+    for y in ys:
+        y.fill_(float("nan"))
+    p.run_unfused()
+    torch.cuda.synchronize()
+    assert same(first, snapshot(ys, lm))
+    p.close()
+
+
 ODD = [(77, 48, 0), (300, 1040, 0), (1, 2048, 1), (129, 272, 2), (64, 1024, 2), (200, 5120, 3)]
 
 

@@ -14,8 +14,9 @@ constexpr int kKeySlots = 16;     // atomic-max slots per lm_head row
 constexpr int kMaxStages = 1024;  // dependency stages of one step
 
 // One NVFP4 matrix of a step.  Items are contiguous blocks of
-// rows_per_item weight rows (all of K); jobs are listed in pass order and
-// their items are numbered consecutively from item_begin.
+// rows_per_item weight rows (all of K) -- or, for a spread job, one K slice
+// of such a block (item = block * slices + slice); jobs are listed in pass
+// order and their items are numbered consecutively from item_begin.
 struct StreamJob {
   const uint8_t* wq;  // [n][k/2]
   const uint8_t* ws;  // [n][k/16]
@@ -30,8 +31,21 @@ struct StreamJob {
   int items;
   int kind;           // 0: GEMM, 1: lm_head (argmax, no output matrix)
   int fmt;            // weight format: 0 NVFP4 (wq codes, ws block scales), 1 FP8 E4M3 (wq [n][k] bytes)
-  int pad[2];         // to a multiple of 16 bytes (the job table is copied in 16-byte pieces)
+  int spread;         // 0, or the K slices of a block dealt as separate items (a step, M >= 2)
+  int part_base;      // spread: first partial slot of the job (StreamArgs::part / part_cnt)
 };
+static_assert(sizeof(StreamJob) % 16 == 0, "the job table is copied in 16-byte pieces");
+
+// K slices of the M >= 2 MFMA item (K % 128 == 0): a block's sum over K is
+// taken slice by slice, each slice summed from zero over its 256-element
+// windows in order, and the slice sums added in slice order.  Whether one
+// workgroup runs every slice or each slice is its own item, the result is
+// the same to the bit.  Slice s covers windows [s*W/S, (s+1)*W/S) of the
+// W = ceil(K/256) windows.
+__host__ __device__ constexpr int lds_windows(int k) { return (k + 255) >> 8; }
+__host__ __device__ constexpr int lds_slices(int k) {
+  return lds_windows(k) / 4 < 1 ? 1 : (lds_windows(k) / 4 > 3 ? 3 : lds_windows(k) / 4);
+}
 
 // Device-side control block of a launch that has an lm_head (argmax keys)
 // or waits on stages.  It must be zero before the first launch; every
@@ -75,6 +89,8 @@ struct StreamArgs {
   int32_t* accept_node;          // [M/T] node whose argmax is the bonus token, or null
   int lm_rows;                   // V of the lm_head job (bounds the token_map lookup)
   int invariant;                 // 1: every M on the MFMA path (row results independent of M)
+  float* part;                   // spread jobs: [slot][M][64] slice sums of a block
+  unsigned* part_cnt;            // spread jobs: [slot] slices done of the block whose slice 0 is that slot
 };
 
 enum StreamMode { STREAM_DIRECT = 0, STREAM_GRID = 1, STREAM_STATIC = 2 };

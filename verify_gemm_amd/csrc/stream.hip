@@ -307,55 +307,82 @@ struct MfmaItem {
 
 // M >= 2, K % 128 == 0: activations shared through LDS.  The four waves
 // split the item's rows -- wave w owns the NT tiles of 16 rows n0 +
-// 16*(NT*w + nt) + c -- and walk K together, one 128-element window at a
-// time.  Every wave loads, P windows ahead, the weights of its own rows and
-// its quarter of the activation window (rows 4*MT*w .. 4*MT*(w+1) - 1 of
-// the 16*MT rows; lanes 16r..16r+15 read the 256 bytes of one row), both
-// into registers with ordinary loads the compiler tracks -- so its waits
-// are exact.  One window before use each wave writes its quarter into an
-// LDS double buffer; after a barrier all waves read the whole window from
-// there: the activations cross the memory path once per workgroup instead
-// of once per wave.  Rows past M load as zeros.
+// 16*(NT*w + nt) + c -- and walk K together, one 256-element window at a
+// time.  Lane (c, gq) holds elements 64*gq .. 64*gq + 63 of the window of
+// its row: 32 contiguous code bytes (two 16-byte loads) and their 4 scale
+// bytes.  The four lanes of a row so read its whole 128-byte line of codes
+// in one window: a CU can keep only so many cache lines in flight, and
+// half-used lines halved the rate.  MFMA step st (0..7) takes elements
+// 64*gq + 8*st .. + 7 of every lane -- a fixed permutation of the window's
+// K positions, which the activations follow, so the sum is still over all
+// of K in a fixed order.
 //
-// LDS layout of a slot: activation row m at byte 256*m; its 16-byte piece
-// q (elements 8q..8q+7 of the window) at position q ^ (m & 15), so that
+// Activations: every wave loads, P windows ahead, 4*MT of the window's
+// 16*MT rows (lanes 32r .. 32r + 31 read the 512 bytes of one row) into
+// registers with ordinary loads the compiler tracks -- so its waits are
+// exact.  One window before use each wave writes them into an LDS double
+// buffer; after a barrier all waves read the whole window from there: the
+// activations cross the memory path once per workgroup instead of once per
+// wave.  Rows past M, and the upper half of a last window when K % 256 ==
+// 128, load as zeros.
+//
+// LDS layout of a slot: activation row m at byte 512*m; its 16-byte piece
+// q (elements 8q .. 8q+7 of the window) at position q ^ (m & 15), so that
 // the 16 lanes reading rows 16*mt + c, piece q, hit 16 different bank
-// groups (and the 16 lanes writing one row hit 16 different ones too).
-// Lane (c, gq) of MFMA step st takes piece 4*gq + st of its row, the same
-// K positions as its weight code dword st.
+// groups (and the 32 lanes writing one row hit 32 different ones).
 template <int MT, int NT, int P>
 struct MfmaLdsItem {
   static constexpr int kRows = 16 * NT * kWaves;
-  static constexpr int kSlotBytes = 16 * MT * 256;
+  static constexpr int kSlotBytes = 16 * MT * 512;
   static constexpr int kRing = 2;  // slots: the window being read, the next one being written
-  u32x4 q[P][NT];
-  unsigned short sc[P][NT];
-  u32x4 xq[P][MT];  // this wave's quarter of the activation window, per ring position
-  f32x4 acc[MT][NT];
+  static constexpr int kXLoads = 2 * MT;  // activation loads per lane per window
+  u32x4 q[P][NT][2];
+  unsigned sc[P][NT];
+  u32x4 xq[P][kXLoads];  // this wave's rows of the activation window, per ring position
+  f32x4 acc[MT][NT];     // the running slice's sum; after compute(), the result (see fold)
+  f32x4 tot[MT][NT];     // sum of the finished slices (whole-block items)
   __amdgpu_buffer_rsrc_t rw[NT], rs[NT], rx;
-  unsigned cw, cs;  // this lane's code / scale byte offset within its tile
-  int n0, nwin;
+  unsigned cw, cs, ew;  // this lane's code / scale byte offset within its tile, element offset in a window
+  int n0, k, nw, ns;    // first row, K, windows of K, K slices
+  int v0, vend, cnt;    // the item's windows [v0, vend), cnt of them
+  int fs, fold_at;      // whole-block items: the running slice and the window its sum ends after
 
-  // Weights are loaded with the default cache policy, not nontemporal: a
-  // window takes 64 bytes of each row's 128-byte line and the next window
-  // the other half, and with the streaming policy the line is often gone
-  // by then (measured: 1.12x the weight bytes fetched against 1.05x, and
-  // the 248,320-row lm_head at M = 17 28 % faster with the default).
+  // Weights are loaded with the default cache policy: the scale bytes of
+  // eight windows share a line, which the streaming policy would evict
+  // before the next window reads it.
   __device__ __forceinline__ void load_w(int p, int v) {
-    const bool in = v < nwin;  // wave-uniform
+    const bool in = v < vend && 256u * (unsigned)v + ew < (unsigned)k;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      q[p][nt] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? cw + 64u * (unsigned)v : kOOB, 0, 0);
-      sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b16(rs[nt], in ? cs + 8u * (unsigned)v : kOOB, 0, 0);
+      const unsigned o = cw + 128u * (unsigned)v;
+      q[p][nt][0] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? o : kOOB, 0, 0);
+      q[p][nt][1] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? o + 16u : kOOB, 0, 0);
+      sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b32(rs[nt], in ? cs + 16u * (unsigned)v : kOOB, 0, 0);
     }
   }
 
-  __device__ __forceinline__ void issue(const StreamJob& j, int item) {
+  // Block `block` of job j: all of K (slice < 0; the slice sums are folded
+  // into tot as they end) or K slice `slice` alone (its sum stays in acc).
+  __device__ __forceinline__ void issue(const StreamJob& j, int block, int slice) {
     const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const unsigned rb = (unsigned)j.k >> 1, sb = (unsigned)j.k >> 4;
-    n0 = item * kRows;
-    nwin = j.k >> 7;
+    n0 = block * kRows;
+    k = j.k;
+    nw = lds_windows(j.k);
+    ns = lds_slices(j.k);
+    if (slice < 0) {
+      v0 = 0;
+      vend = nw;
+      fs = 0;
+      fold_at = nw / ns;
+    } else {
+      v0 = slice * nw / ns;
+      vend = (slice + 1) * nw / ns;
+      fs = ns;
+      fold_at = -1;  // never
+    }
+    cnt = vend - v0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int t0 = n0 + 16 * (NT * w + nt);
@@ -363,50 +390,55 @@ struct MfmaLdsItem {
       rw[nt] = rsrc_uniform(j.wq + (size_t)t0 * rb, (unsigned)rows * rb);
       rs[nt] = rsrc_uniform(j.ws + (size_t)t0 * sb, (unsigned)rows * sb);
     }
-    cw = (unsigned)c * rb + 16u * (unsigned)gq;
-    cs = (unsigned)c * sb + 2u * (unsigned)gq;
+    cw = (unsigned)c * rb + 32u * (unsigned)gq;
+    cs = (unsigned)c * sb + 4u * (unsigned)gq;
+    ew = 64u * (unsigned)gq;
 #pragma unroll
-    for (int p = 0; p < P; ++p) load_w(p, p);
+    for (int p = 0; p < P; ++p) load_w(p, v0 + p);
   }
 
-  // Row of this lane's activation piece i (wave w's quarter).
+  // Row of this lane's activation load i (wave w's rows).
   __device__ __forceinline__ int xrow(int i) const {
-    return 4 * (MT * (int)(threadIdx.x >> 6) + i) + ((threadIdx.x & 63) >> 4);
+    return 2 * (kXLoads * (int)(threadIdx.x >> 6) + i) + ((threadIdx.x & 63) >> 5);
   }
 
-  __device__ __forceinline__ void load_x(int p, int v, int k) {
-    const unsigned piece = threadIdx.x & 15;
-    const bool in = v < nwin;
+  __device__ __forceinline__ void load_x(int p, int v) {
+    const unsigned piece = threadIdx.x & 31;
+    const unsigned e = 256u * (unsigned)v + 8u * piece;
+    const bool in = v < vend && e < (unsigned)k;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const unsigned off = (unsigned)xrow(i) * (unsigned)k * 2u + 256u * (unsigned)v + 16u * piece;
+    for (int i = 0; i < kXLoads; ++i) {
+      const unsigned off = ((unsigned)xrow(i) * (unsigned)k + e) * 2u;
       xq[p][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? off : kOOB, 0, 0);
     }
   }
 
   __device__ __forceinline__ void store_x(int p, unsigned char* slot) {
-    const unsigned piece = threadIdx.x & 15;
+    const unsigned piece = threadIdx.x & 31;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    for (int i = 0; i < kXLoads; ++i) {
       const int m = xrow(i);
-      *reinterpret_cast<u32x4*>(slot + 256 * m + 16 * (piece ^ (unsigned)(m & 15))) = xq[p][i];
+      *reinterpret_cast<u32x4*>(slot + 512 * m + 16 * (piece ^ (unsigned)(m & 15))) = xq[p][i];
     }
   }
 
   __device__ __forceinline__ void window(int p, const unsigned char* slot) {
     const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+    f32x2 s[NT][2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int nt = 0; nt < NT; ++nt) {
+      s[nt][0] = e4m3x2_lo((unsigned short)(sc[p][nt] & 0xFFFFu));
+      s[nt][1] = e4m3x2_lo((unsigned short)(sc[p][nt] >> 16));
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
       bf16x8 b[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const f32x2 s = e4m3x2_lo(sc[p][nt]);
-        b[nt] = dequant8_bf16(q[p][nt][st], st < 2 ? s[0] : s[1]);
-      }
+      for (int nt = 0; nt < NT; ++nt) b[nt] = dequant8_bf16(q[p][nt][st >> 2][st & 3], s[nt][st >> 2][(st >> 1) & 1]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = 16 * mt + c;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(slot + 256 * m + 16 * ((4 * gq + st) ^ c));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(slot + 512 * m + 16 * ((8 * gq + st) ^ c));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b[nt],
@@ -420,11 +452,14 @@ struct MfmaLdsItem {
   __device__ __forceinline__ void compute(const StreamJob& j, int M, unsigned char* lds) {
     rx = rsrc_uniform(j.x, (unsigned)M * (unsigned)j.k * 2u);
 #pragma unroll
-    for (int p = 0; p < P; ++p) load_x(p, p, j.k);
+    for (int p = 0; p < P; ++p) load_x(p, v0 + p);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        tot[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     store_x(0, lds);
     // The loop over whole groups of P windows must be entered in the order
     // its own iterations leave the loads in, and contain no skipped step:
@@ -435,29 +470,52 @@ struct MfmaLdsItem {
     // group is peeled off, the loop runs whole groups only, and the last,
     // partial group (or all of a short K) is done step by step.
     int base = 0;
-    if (nwin >= 2 * P) {
+    if (cnt >= 2 * P) {
 #pragma unroll
-      for (int p = 0; p < P; ++p) step(p, p, j.k, lds);
-      for (base = P; base + P <= nwin; base += P) {
+      for (int p = 0; p < P; ++p) step(p, p, lds);
+      for (base = P; base + P <= cnt; base += P) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) step(p, base + p, j.k, lds);
+        for (int p = 0; p < P; ++p) step(p, base + p, lds);
       }
     }
-    for (; base < nwin; base += P) {
+    for (; base < cnt; base += P) {
 #pragma unroll
       for (int p = 0; p < P; ++p)
-        if (base + p < nwin) step(p, base + p, j.k, lds);
+        if (base + p < cnt) step(p, base + p, lds);
+    }
+    if (fold_at >= 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = tot[mt][nt];
     }
   }
 
-  // Window v (ring position p = v % P): compute it, pass the next window's
-  // activations to LDS, and load window v + P into position p.
-  __device__ __forceinline__ void step(int p, int v, int k, unsigned char* lds) {
-    __syncthreads();  // window v is in LDS; every wave is done with window v-1
-    window(p, lds + (v & 1) * kSlotBytes);
-    store_x(p + 1 < P ? p + 1 : 0, lds + ((v + 1) & 1) * kSlotBytes);
-    load_x(p, v + P, k);
-    load_w(p, v + P);
+  // A slice ended (whole-block items): tot += its sum, in slice order from
+  // +0.0 -- the order in which a spread block's partials are added.
+  __device__ __forceinline__ void fold() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[mt][nt][r] = tot[mt][nt][r] + acc[mt][nt][r];
+        acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    ++fs;
+    fold_at = (fs + 1) * nw / ns;
+  }
+
+  // The item's window i (window v0 + i of K; ring position p = i % P):
+  // compute it, pass the next window's activations to LDS, and load window
+  // v0 + i + P into position p.
+  __device__ __forceinline__ void step(int p, int i, unsigned char* lds) {
+    __syncthreads();  // window i is in LDS; every wave is done with window i-1
+    window(p, lds + (i & 1) * kSlotBytes);
+    if (v0 + i + 1 == fold_at) fold();
+    store_x(p + 1 < P ? p + 1 : 0, lds + ((i + 1) & 1) * kSlotBytes);
+    load_x(p, v0 + i + P);
+    load_w(p, v0 + i + P);
   }
 };
 
@@ -683,7 +741,7 @@ struct Cfg {
   static constexpr bool XPF = MT <= 2;         // prefetch the next window's activations
   // the LDS-shared item (K % 128 == 0): 16-row tiles per wave, window ring depth
   static constexpr int LNT = 1;
-  static constexpr int LP = MT <= 2 ? 6 : 4;
+  static constexpr int LP = MT <= 2 ? 4 : 2;
   using Lds = MfmaLdsItem<MT, LNT, LP>;
 };
 
@@ -764,43 +822,93 @@ __device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item,
     }
 }
 
-// The LDS-shared MFMA item: each wave finishes its own rows (no reduction).
+// Where a spread job's slice sums meet (STATIC launches; null elsewhere).
+struct SpreadCtx {
+  float* part;
+  unsigned* cnt;
+  int* flag;  // an LDS word
+};
+
+__device__ __forceinline__ float ld_agent_f(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The LDS-shared MFMA item: each wave finishes its own rows (no reduction
+// across waves).  A whole-block item stores (or offers) its rows.  A slice
+// of a spread job stores its slice sum to its partial slot and counts
+// itself in; the workgroup that completes the block adds the slice sums
+// from +0.0 in slice order -- as a whole-block item folds them -- and
+// finishes the rows, then clears the count for the next launch.
 template <int MT, class Dep, class BestT>
 __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M, Dep&& dep, unsigned char* xring,
-                                             BestT& best) {
+                                             const SpreadCtx& sp, BestT& best) {
   using Item = typename Cfg<MT>::Lds;
   constexpr int NT = Cfg<MT>::LNT;
+  static_assert(NT == 1, "one 16-row tile per wave");
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4, w = threadIdx.x >> 6;
+  const int S = j.spread;
+  const int block = S ? item / S : item, slice = S ? item - block * S : -1;
   Item it;
-  it.issue(j, item);
-  float rsc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rsc[nt] = row_scale(j, it.n0 + 16 * (NT * w + nt) + c);
+  it.issue(j, block, slice);
+  const int n = it.n0 + 16 * w + c;
+  const float rsc = row_scale(j, n);
   const bool ok = dep();
   it.compute(j, M, xring);
+  if (S) {
+    float* mine = sp.part + (size_t)(j.part_base + item) * (size_t)M * 64u;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * mt + 4 * gq + r;
+        if (m < M) store_out(&mine[m * 64 + 16 * w + c], it.acc[mt][0][r]);
+      }
+    // The slice sums are agent-coherent stores and the count is taken once
+    // they have completed (vmcnt(0)), as a stage is signalled; the
+    // completing workgroup reads them with agent-coherent loads.  No cache
+    // write-back or invalidation is needed -- a fence here costs every
+    // slice item an L2 write-back.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    unsigned* count = &sp.cnt[j.part_base + block * S];
+    if (threadIdx.x == 0)
+      *sp.flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
+    __syncthreads();
+    const bool last = *sp.flag != 0;
+    __syncthreads();
+    if (!last) return;
+    const float* first = sp.part + (size_t)(j.part_base + block * S) * (size_t)M * 64u;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * mt + 4 * gq + r;
+        if (m < M) {
+          float t = 0.0f;
+          for (int q = 0; q < S; ++q)
+            t = t + (q == slice ? it.acc[mt][0][r] : ld_agent_f(&first[((size_t)q * M + m) * 64 + 16 * w + c]));
+          it.acc[mt][0][r] = t;
+        }
+      }
+    if (threadIdx.x == 0) st_agent(count, 0u);
+  }
   if (!ok) return;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mt + 4 * gq + r;
-      if (m < M) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int n = it.n0 + 16 * (NT * w + nt) + c;
-          if (n < j.n) {
-            const float v = it.acc[mt][nt][r] * j.g * rsc[nt];
-            if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], v);
-            else best.offer(mt * 4 + r, v, n);
-          }
-        }
+      if (m < M && n < j.n) {
+        const float v = it.acc[mt][0][r] * j.g * rsc;
+        if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], v);
+        else best.offer(mt * 4 + r, v, n);
       }
     }
 }
 
 template <int MT, class Dep, class BestT>
 __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, Dep&& dep, float* red,
-                                         unsigned char* xring, BestT& best) {
+                                         unsigned char* xring, const SpreadCtx& sp, BestT& best) {
   if constexpr (MT == 0) {
     if (j.fmt == 1) gemv_generic_run<Fp8GemvItem>(j, item, dep, best);
     else if (j.k == 5120) gemv_run<5, 4>(j, item, dep, best);
@@ -813,7 +921,7 @@ __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, De
       Fp8MfmaItem<MT, NT> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
     } else if ((j.k & 127) == 0) {
-      mfma_lds_run<MT>(j, item, M, dep, xring, best);
+      mfma_lds_run<MT>(j, item, M, dep, xring, sp, best);
     } else {
       MfmaGuardedItem<MT, NT> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
@@ -942,11 +1050,13 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
 
   if constexpr (MODE == MODE_DIRECT) {
     auto nodep = [] { return true; };
-    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, best);
+    const SpreadCtx nosp{nullptr, nullptr, nullptr};
+    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, nosp, best);
     return;
   } else {
     StreamCtl* ctl = a.ctl;
     const int G = gridDim.x;
+    const SpreadCtx sp{a.part, a.part_cnt, &lds_flag};
     int cur = 0;          // job cursor (items only grow)
     int done_stage = -1;  // highest stage known complete
     int my_stage = -1;    // stage of the items this workgroup is working on
@@ -982,7 +1092,7 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
         }
         return true;
       };
-      run_item<MT>(j, item, a.M, dep, red, xring, best);
+      run_item<MT>(j, item, a.M, dep, red, xring, sp, best);
       // LDS reuse by the next item (M >= 2: its activation copies go into
       // ring slots the slowest wave may still be reading)
       if constexpr (MODE == MODE_STATIC || MT > 0) __syncthreads();
