@@ -114,22 +114,45 @@ def test_one_layer_step(M, T):
     p.close()
 
 
-SPREAD = [(1280, 17408, 0), (333, 5120, 1), (4096, 1024, 2)]
+SPREAD = [(1280, 17408, 0), (333, 5120, 1), (4096, 1024, 2), (16640, 5120, 3)]
+
+
+def sliced_items(blocks, k, grid):
+    """Items of a one-job stage of `blocks` 64-row blocks under the step's
+    slicing rule: S = clamp(W // 4, 1, 3) slices of the W = ceil(K/256)
+    windows; all blocks sliced when fewer than the grid and estimated faster,
+    else the blocks past the last whole round."""
+    w = -(-k // 256)
+    s = min(3, max(1, w // 4))
+    whole = -(-blocks // grid) * w
+    slice_w = -(-w // s) + 1
+    cut = 0
+    if s > 1:
+        if blocks < grid:
+            cut = blocks if -(-(blocks * s) // grid) * slice_w * 5 < whole * 4 else 0
+        elif blocks % grid:
+            r = blocks % grid
+            cut = r if blocks // grid * w + -(-(r * s) // grid) * slice_w < whole else 0
+    return blocks + cut * (s - 1)
 
 
 @pytest.mark.parametrize("M", [2, 17, 68])
 def test_spread_slices(M):
-    """Narrow matrices at M >= 2 are dealt as K slices of 64-row blocks, one
-    item per slice, the slice sums added in slice order by the workgroup
-    that completes a block.  The item count shows which stages are spread
-    (1280 x 17408: 20 blocks x 3 slices; 333 x 5120: 6 x 3; 4096 x 1024:
-    one slice, 64 blocks; lm_head 1000 x 2048: 16 x 2); the bits equal the
-    one-launch-per-matrix schedule, where one workgroup runs every slice of
-    a block; repeated launches (the per-block counts reset themselves) give
-    the same bits; every output is within the oracle's bound."""
+    """The step deals blocks of the M >= 2 MFMA item as K slices, one item
+    per slice, where that balances a stage better: every block of a narrow
+    matrix (1280 x 17408, 333 x 5120; 4096 x 1024 has K too short to slice;
+    the lm_head 1000 x 2048), or only the blocks past the last whole round
+    of a wide one (16640 x 5120: 260 blocks).  The slice sums are added in
+    slice order by the workgroup that completes a block.  The item count
+    shows the schedule; the bits equal the one-launch-per-matrix schedule,
+    where one workgroup runs every slice of a block; repeated launches (the
+    per-block counts reset themselves) give the same bits; every output is
+    within the oracle's bound."""
     print(f"[case] spread slices M={M}", flush=True)
     p, host, ys, lm, lmhost = build(M, 1, SPREAD, (1000, 2048), 33000 + M)
-    assert p.info()["items"] == 60 + 18 + 64 + 32
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    want = sum(sliced_items(-(-n // 64), k, grid) for n, k, _ in SPREAD) + sliced_items(-(-1000 // 64), 2048, grid)
+    assert p.info()["items"] == want
     p.run()
     torch.cuda.synchronize()
     assert p.check() == 0

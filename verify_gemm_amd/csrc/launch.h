@@ -14,9 +14,10 @@ constexpr int kKeySlots = 16;     // atomic-max slots per lm_head row
 constexpr int kMaxStages = 1024;  // dependency stages of one step
 
 // One NVFP4 matrix of a step.  Items are contiguous blocks of
-// rows_per_item weight rows (all of K) -- or, for a spread job, one K slice
-// of such a block (item = block * slices + slice); jobs are listed in pass
-// order and their items are numbered consecutively from item_begin.
+// rows_per_item weight rows (all of K) -- or, from a spread job's first
+// spread block f on, one K slice of such a block (item f + (b - f) * S + s
+// is slice s of block b, S = lds_slices(k)); jobs are listed in pass order
+// and their items are numbered consecutively from item_begin.
 struct StreamJob {
   const uint8_t* wq;  // [n][k/2]
   const uint8_t* ws;  // [n][k/16]
@@ -31,8 +32,8 @@ struct StreamJob {
   int items;
   int kind;           // 0: GEMM, 1: lm_head (argmax, no output matrix)
   int fmt;            // weight format: 0 NVFP4 (wq codes, ws block scales), 1 FP8 E4M3 (wq [n][k] bytes)
-  int spread;         // 0, or the K slices of a block dealt as separate items (a step, M >= 2)
-  int part_base;      // spread: first partial slot of the job (StreamArgs::part / part_cnt)
+  int spread;         // 0, or 1 + the first block whose K slices are separate items (a step, M >= 2)
+  int part_base;      // spread: partial slot of the job's first slice item (StreamArgs::part / part_cnt)
 };
 static_assert(sizeof(StreamJob) % 16 == 0, "the job table is copied in 16-byte pieces");
 
@@ -98,6 +99,8 @@ enum StreamMode { STREAM_DIRECT = 0, STREAM_GRID = 1, STREAM_STATIC = 2 };
 // 0 for the M = 1 GEMV path, else the number of 16-row M-tiles.  A batch-
 // invariant launch never takes the GEMV path (M = 1 runs as one M-tile).
 int stream_mt_class(int M, bool invariant);
+// Rows of a block of the LDS-shared MFMA item (M >= 2 or batch-invariant).
+int stream_lds_rows(int M, bool invariant);
 // Weight rows per item for a batch of M rows and a reduction length K.
 int stream_rows_per_item(int M, int K, bool invariant, int fmt);
 // DIRECT: grid = items of a.job0.  GRID: a.job0 walked by up to `grid`

@@ -711,6 +711,11 @@ struct Best {
   }
 };
 
+// Items of GEMM jobs keep no running best.
+struct NoBest {
+  __device__ __forceinline__ void offer(int, float, int) {}
+};
+
 __device__ __forceinline__ void publish_best(StreamCtl* ctl, int m, float v, int idx) {
   if (idx < 0) return;
   const int slot = blockIdx.x % kKeySlots;
@@ -843,25 +848,29 @@ template <int MT, class Dep, class BestT>
 __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M, Dep&& dep, unsigned char* xring,
                                              const SpreadCtx& sp, BestT& best) {
   using Item = typename Cfg<MT>::Lds;
-  constexpr int NT = Cfg<MT>::LNT;
-  static_assert(NT == 1, "one 16-row tile per wave");
+  constexpr int NT = Cfg<MT>::LNT, R = Item::kRows;
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4, w = threadIdx.x >> 6;
-  const int S = j.spread;
-  const int block = S ? item / S : item, slice = S ? item - block * S : -1;
+  const int S = lds_slices(j.k), first = j.spread - 1;
+  const bool sliced = j.spread && item >= first;
+  const int t = item - first;  // this slice item's number within the job's slice items
+  const int block = sliced ? first + t / S : item, slice = sliced ? t - (t / S) * S : -1;
   Item it;
   it.issue(j, block, slice);
-  const int n = it.n0 + 16 * w + c;
-  const float rsc = row_scale(j, n);
+  float rsc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rsc[nt] = row_scale(j, it.n0 + 16 * (NT * w + nt) + c);
   const bool ok = dep();
   it.compute(j, M, xring);
-  if (S) {
-    float* mine = sp.part + (size_t)(j.part_base + item) * (size_t)M * 64u;
+  if (sliced) {
+    float* mine = sp.part + (size_t)(j.part_base + t) * (size_t)M * R;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * mt + 4 * gq + r;
-        if (m < M) store_out(&mine[m * 64 + 16 * w + c], it.acc[mt][0][r]);
+        if (m < M)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) store_out(&mine[m * R + 16 * (NT * w + nt) + c], it.acc[mt][nt][r]);
       }
     // The slice sums are agent-coherent stores and the count is taken once
     // they have completed (vmcnt(0)), as a stage is signalled; the
@@ -870,25 +879,29 @@ __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M
     // slice item an L2 write-back.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    unsigned* count = &sp.cnt[j.part_base + block * S];
+    const int slot0 = j.part_base + (block - first) * S;  // the block's slice 0
+    unsigned* count = &sp.cnt[slot0];
     if (threadIdx.x == 0)
       *sp.flag = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
     __syncthreads();
     const bool last = *sp.flag != 0;
     __syncthreads();
     if (!last) return;
-    const float* first = sp.part + (size_t)(j.part_base + block * S) * (size_t)M * 64u;
+    const float* p0 = sp.part + (size_t)slot0 * (size_t)M * R;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * mt + 4 * gq + r;
-        if (m < M) {
-          float t = 0.0f;
-          for (int q = 0; q < S; ++q)
-            t = t + (q == slice ? it.acc[mt][0][r] : ld_agent_f(&first[((size_t)q * M + m) * 64 + 16 * w + c]));
-          it.acc[mt][0][r] = t;
-        }
+        if (m < M)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int col = 16 * (NT * w + nt) + c;
+            float sum = 0.0f;
+            for (int q = 0; q < S; ++q)
+              sum = sum + (q == slice ? it.acc[mt][nt][r] : ld_agent_f(&p0[((size_t)q * M + m) * R + col]));
+            it.acc[mt][nt][r] = sum;
+          }
       }
     if (threadIdx.x == 0) st_agent(count, 0u);
   }
@@ -898,10 +911,14 @@ __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mt + 4 * gq + r;
-      if (m < M && n < j.n) {
-        const float v = it.acc[mt][0][r] * j.g * rsc;
-        if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], v);
-        else best.offer(mt * 4 + r, v, n);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = it.n0 + 16 * (NT * w + nt) + c;
+        if (m < M && n < j.n) {
+          const float v = it.acc[mt][nt][r] * j.g * rsc[nt];
+          if (j.kind == 0) store_out(&j.y[(size_t)m * j.n + n], v);
+          else best.offer(mt * 4 + r, v, n);
+        }
       }
     }
 }
@@ -1045,13 +1062,11 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
   __shared__ int lds_flag;
   __shared__ int lds_am[VG_MAX_M_DEV];
   __shared__ int lds_dep[VG_MAX_M_DEV];
-  Best<MT == 0 ? 1 : MT * 4> best;
-  best.init();
-
   if constexpr (MODE == MODE_DIRECT) {
     auto nodep = [] { return true; };
     const SpreadCtx nosp{nullptr, nullptr, nullptr};
-    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, nosp, best);
+    NoBest nobest;
+    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, nosp, nobest);
     return;
   } else {
     StreamCtl* ctl = a.ctl;
@@ -1060,16 +1075,21 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
     int cur = 0;          // job cursor (items only grow)
     int done_stage = -1;  // highest stage known complete
     int my_stage = -1;    // stage of the items this workgroup is working on
-    for (int t = blockIdx.x; t < a.total_items; t += G) {
+    // Items of the GEMM jobs, then those of the lm_head (the last job of a
+    // step, every job of a GRID launch): the lm_head's running best is live
+    // only in the second loop, not across the whole step.
+    const int lm_begin = MODE == MODE_GRID ? 0 : (a.has_lmhead ? a.jobs[a.njobs - 1].item_begin : a.total_items);
+    int t = blockIdx.x;
+    auto body = [&](int ti, auto& best) {
       const StreamJob* jp;
       if constexpr (MODE == MODE_GRID) {
         jp = &a.job0;
       } else {
-        while (cur + 1 < a.njobs && a.jobs[cur + 1].item_begin <= t) ++cur;
+        while (cur + 1 < a.njobs && a.jobs[cur + 1].item_begin <= ti) ++cur;
         jp = &a.jobs[cur];
       }
       const StreamJob j = *jp;
-      const int item = t - j.item_begin;
+      const int item = ti - j.item_begin;
       if constexpr (MODE == MODE_STATIC) {
         if (j.stage != my_stage) {
           // leaving a stage: one signal for all of this workgroup's items in it
@@ -1096,7 +1116,14 @@ __global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
       // LDS reuse by the next item (M >= 2: its activation copies go into
       // ring slots the slowest wave may still be reading)
       if constexpr (MODE == MODE_STATIC || MT > 0) __syncthreads();
+    };
+    {
+      NoBest nobest;
+      for (; t < lm_begin; t += G) body(t, nobest);
     }
+    Best<MT == 0 ? 1 : MT * 4> best;
+    best.init();
+    for (; t < a.total_items; t += G) body(t, best);
     if constexpr (MODE == MODE_STATIC) {
       if (my_stage >= 0) signal_stage(a, my_stage);
     }
@@ -1160,6 +1187,16 @@ hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream
 
 int stream_mt_class(int M, bool invariant) { return M == 1 && !invariant ? 0 : (M + 15) / 16; }
 
+int stream_lds_rows(int M, bool invariant) {
+  switch (stream_mt_class(M, invariant)) {
+    case 1: return Cfg<1>::Lds::kRows;
+    case 2: return Cfg<2>::Lds::kRows;
+    case 3: return Cfg<3>::Lds::kRows;
+    case 4: return Cfg<4>::Lds::kRows;
+    default: return Cfg<5>::Lds::kRows;
+  }
+}
+
 int stream_rows_per_item(int M, int K, bool invariant, int fmt) {
   const int mt = stream_mt_class(M, invariant);
   if (mt == 0 && fmt == 1) return Fp8GemvItem::kRows;
@@ -1169,7 +1206,7 @@ int stream_rows_per_item(int M, int K, bool invariant, int fmt) {
     if (K == 1024) return GemvItem<1, 8>::kRows;
     return GemvGenericItem::kRows;
   }
-  if (fmt == 0 && (K & 127) == 0) return Cfg<1>::Lds::kRows;  // the LDS-shared item (same rows for every MT)
+  if (fmt == 0 && (K & 127) == 0) return stream_lds_rows(M, invariant);
   return 16 * (mt <= 2 ? 2 : 4);
 }
 
