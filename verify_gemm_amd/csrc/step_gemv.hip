@@ -28,6 +28,13 @@
 //   * one STORE wave stores the results the compute waves left in LDS and
 //     signals a stage once its results are stored and complete.
 //
+// At a stage boundary the compute waves hold back the next stage's first
+// chunk until the store wave has signalled the stage: a CU's vector memory
+// operations queue in order, and with that chunk's loads issued first the
+// result stores and the signal waited behind ~100 KB of weight loads
+// (measured: the pass 6 % faster this way).  The loads still have the whole
+// stage wait to arrive in.
+//
 // The roles hand over through LDS counters, not barriers: the I/O wave
 // releases chunk k once its activations and scales are in LDS; each
 // compute wave counts the chunks it has finished; the store wave counts
@@ -162,6 +169,7 @@ struct Shared {
   unsigned done[2];                  // compute waves finished with the chunk of that parity
   unsigned ready;                    // chunks released to the compute waves
   unsigned flushed;                  // chunks whose results are stored (all areas they used are free)
+  unsigned signalled;                // 1 + the last stage this workgroup has signalled
   int flag;
 };
 
@@ -420,6 +428,12 @@ __device__ __forceinline__ void work(Shared& sh, const Chunk& ch, int w, const B
     __hip_atomic_fetch_add(&sh.done[parity], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Waits until the store wave has signalled stage s - 1.  It does once every
+// compute wave has finished that stage's chunks, which the caller has.
+__device__ __forceinline__ void wait_signalled(const Shared& sh, unsigned s) {
+  while (lds_load(&sh.signalled) < s) __builtin_amdgcn_s_sleep(1);
+}
+
 __device__ __forceinline__ void compute_loop(const StreamArgs& a, Shared& sh, int njobs, float& best_v,
                                              int& best_i) {
   // the wave index, known to the compiler as wave-uniform (scalar): buffer
@@ -442,16 +456,28 @@ __device__ __forceinline__ void compute_loop(const StreamArgs& a, Shared& sh, in
   for (;;) {
     bool more = next_chunk(sh, njobs, cu, nxt);
     if (!more) nxt = Chunk{cur.job, 0, 0};
-    issue(lds_job(sh, nxt.job), nxt, w, b1);
+    int cst = lds_job(sh, cur.job).stage;
+    bool defer = a.waits && more && lds_job(sh, nxt.job).stage != cst;
+    if (!defer) issue(lds_job(sh, nxt.job), nxt, w, b1);
     wait_ready(sh, k++);
     work(sh, cur, w, b0, 0, sidx, ep, best_v, best_i);
+    if (defer) {
+      wait_signalled(sh, (unsigned)cst + 1u);
+      issue(lds_job(sh, nxt.job), nxt, w, b1);
+    }
     if (!more) break;
     cur = nxt;
     more = next_chunk(sh, njobs, cu, nxt);
     if (!more) nxt = Chunk{cur.job, 0, 0};
-    issue(lds_job(sh, nxt.job), nxt, w, b0);
+    cst = lds_job(sh, cur.job).stage;
+    defer = a.waits && more && lds_job(sh, nxt.job).stage != cst;
+    if (!defer) issue(lds_job(sh, nxt.job), nxt, w, b0);
     wait_ready(sh, k++);
     work(sh, cur, w, b1, 1, sidx, ep, best_v, best_i);
+    if (defer) {
+      wait_signalled(sh, (unsigned)cst + 1u);
+      issue(lds_job(sh, nxt.job), nxt, w, b0);
+    }
     if (!more) break;
     cur = nxt;
   }
@@ -657,7 +683,10 @@ __device__ __forceinline__ void store_loop(const StreamArgs& a, Shared& sh, int 
     // the LDS reads of the flush have completed before the areas are handed back
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if ((threadIdx.x & 63) == 0) lds_store(&sh.flushed, k + 1);
-    if (a.waits && (!more || lds_job(sh, nxt.job).stage != j.stage)) signal_stage(a, j.stage);
+    if (a.waits && (!more || lds_job(sh, nxt.job).stage != j.stage)) {
+      signal_stage(a, j.stage);
+      if ((threadIdx.x & 63) == 0) lds_store(&sh.signalled, (unsigned)j.stage + 1u);
+    }
     if (!more) break;
     cur = nxt;
     parity ^= 1;
@@ -681,6 +710,7 @@ __global__ __launch_bounds__(kWG) void step_gemv_kernel(StreamArgs a) {
   if (threadIdx.x == 0) {
     sh.ready = 0;
     sh.flushed = 0;
+    sh.signalled = 0;
   }
   __syncthreads();
 
