@@ -150,9 +150,11 @@ def test_spread_slices(M):
     within the oracle's bound."""
     print(f"[case] spread slices M={M}", flush=True)
     p, host, ys, lm, lmhost = build(M, 1, SPREAD, (1000, 2048), 33000 + M)
-    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    info = p.info()
+    grid = info["grid"]
+    assert grid >= torch.cuda.get_device_properties(0).multi_processor_count
     want = sum(sliced_items(-(-n // 64), k, grid) for n, k, _ in SPREAD) + sliced_items(-(-1000 // 64), 2048, grid)
-    assert p.info()["items"] == want
+    assert info["items"] == want
     p.run()
     torch.cuda.synchronize()
     assert p.check() == 0

@@ -58,6 +58,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "vg_pass_run_unfused": (i32, [vp, vp]),
         "vg_pass_check": (i32, [vp, ctypes.POINTER(i32)]),
         "vg_pass_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+        "vg_pass_grid": (i32, [vp, ctypes.POINTER(i32)]),
         "vg_pass_destroy": (None, [vp]),
         "nvfp4_gemm_invariant": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp]),
         "lmhead_verify": (i32, [vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -410,7 +411,9 @@ class Pass:
         a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
         _check(self._lib.vg_pass_info(self.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
                "vg_pass_info")
-        return {"jobs": a.value, "stages": b.value, "items": c.value}
+        g = ctypes.c_int()
+        _check(self._lib.vg_pass_grid(self.handle, ctypes.byref(g)), "vg_pass_grid")
+        return {"jobs": a.value, "stages": b.value, "items": c.value, "grid": g.value}
 
     def close(self):
         if getattr(self, "handle", None):

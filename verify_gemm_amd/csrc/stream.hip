@@ -1053,7 +1053,11 @@ __device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am, 
 }
 
 template <int MT, int MODE>
-__global__ __launch_bounds__(kWG) void stream_kernel(StreamArgs a) {
+// Two M-tiles: registers capped for two waves per SIMD, so the step can
+// keep two workgroups per CU (measured: the M = 17 step 4 % faster; one
+// M-tile and three or more gain nothing or lose).
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2 : 1))) void stream_kernel(
+    StreamArgs a) {
   constexpr int NT = MT == 0 ? 1 : Cfg<MT>::NT;
   constexpr int kRed = MT == 0 ? 1 : (kWaves - 1) * MT * NT * 4 * kWave;
   __shared__ float red[kRed];
@@ -1212,8 +1216,8 @@ int stream_rows_per_item(int M, int K, bool invariant, int fmt) {
 
 int stream_static_grid(int M, bool invariant) {
   // All workgroups must be resident (the static schedule waits on them);
-  // one per CU measured best: more only park more prefetched items behind
-  // the stage waits.
+  // one per CU measured best except with two M-tiles, where two per CU
+  // (the kernel's registers allow it) keep more items in flight.
   int cap = 0;
   switch (stream_mt_class(M, invariant)) {
     case 0: cap = resident_blocks<0, MODE_STATIC>(); break;
@@ -1223,7 +1227,8 @@ int stream_static_grid(int M, bool invariant) {
     case 4: cap = resident_blocks<4, MODE_STATIC>(); break;
     default: cap = resident_blocks<5, MODE_STATIC>(); break;
   }
-  return cap < num_cus() ? cap : num_cus();
+  const int want = (stream_mt_class(M, invariant) == 2 ? 2 : 1) * num_cus();
+  return cap < want ? cap : want;
 }
 
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
