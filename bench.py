@@ -2,8 +2,11 @@
 
 One step = one pass over the whole hot path: 64 layers x {q, k, v, o, gate,
 up, down} NVFP4 GEMMs + the lm_head with fused argmax and greedy accept
-(449 matrices, 14,115,962,880 weight bytes), run as ONE persistent kernel
-launch of the native step executor (vg_pass_run).  Each layer's q, k, v (and
+(449 matrices, 14,115,962,880 weight bytes), run by the native step
+executor (vg_pass_run) in its faster schedule: ONE persistent kernel launch
+at M = 1, one launch per job at M >= 2 (there the hardware dispatcher
+balances each matrix's blocks; the persistent launch is timed beside it as
+``persistent_us_per_pass``).  Each layer's q, k, v (and
 gate, up) are stored back to back and read as one stacked matrix -- 257 jobs
 -- with each member's own tensor scale kept as per-row scales, so every
 output has the same bits as with 449 separate jobs (the fused projections
@@ -164,7 +167,7 @@ def main():
         # The timed step: every layer's {q,k,v} and {gate,up} read as one
         # stacked matrix each (257 jobs), each member keeping its own tensor
         # scale as per-row scales -- the same bytes and the same output bits
-        # as 449 separate jobs -- in one persistent launch.
+        # as 449 separate jobs -- in vg_pass_run's schedule for this M.
         run = weightpass.PassRun(weights, M, fused=True)
         run.run()
         torch.cuda.synchronize()
@@ -176,7 +179,12 @@ def main():
         gbps = wbytes / (ms * 1e-3) / 1e9
         entry = {"us_per_pass": round(ms * 1000, 2), "weight_gbps": round(gbps, 1),
                  "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-                 "pct_of_probe": round(100 * gbps / probe, 2), "jobs": run.step.info()["jobs"]}
+                 "pct_of_probe": round(100 * gbps / probe, 2), "jobs": run.step.info()["jobs"],
+                 "schedule": "one persistent launch" if M == 1 else "one launch per job"}
+        if M != 1:
+            entry["persistent_us_per_pass"] = round(time_launches(run.run_persistent, args.steps, args.warmup) * 1000, 2)
+            if run.check():
+                raise RuntimeError(f"M={M}: a stage wait timed out in the persistent launch")
         if not args.no_unfused:
             reps = max(2, min(args.steps, 5))
             g = run.capture_unfused()
@@ -203,7 +211,10 @@ def main():
         torch.cuda.empty_cache()
     head = per_m[str(ms_list[0])]
     kus = head["us_per_pass"]
-    achieved = wbytes / (kus * 1e-6) / 1e9
+    # the roofline is that of one launch of the whole step: at M >= 2 the
+    # persistent launch timed beside the per-job schedule
+    lus = head.get("persistent_us_per_pass", kus)
+    achieved = wbytes / (lus * 1e-6) / 1e9
     out = {
         "metric": "µs per full weight pass + effective weight GB/s (% HBM peak) at M=1/17/68",
         "value": head["weight_gbps"],
@@ -219,7 +230,8 @@ def main():
         "data": "synthetic (seeded device RNG, codes uniform, scales 2^u)",
         "config": {"workload": "full synthetic weight pass: 64 layers x {q,k,v,o 5120x5120; gate,up "
                                "17408x5120; down 5120x17408} + lm_head 248320x5120 with argmax/accept "
-                               f"(449 NVFP4 matrices, {wbytes} weight bytes), one persistent launch per pass; "
+                               f"(449 NVFP4 matrices, {wbytes} weight bytes), one persistent launch per pass at "
+                               "M=1 (one launch per job at M>=2); "
                                "each layer's q|k|v and gate|up read as one stacked matrix (257 jobs, per-matrix "
                                "tensor scales kept as per-row scales, outputs bit-identical to 449 jobs)",
                    "M": ms_list[0], "M_reported": ms_list},
@@ -230,7 +242,7 @@ def main():
                      "traffic": recorded_traffic(step_kernel_name(ms_list[0])),
                      "kernel": (f"{step_kernel_name(ms_list[0])} (the whole step is one launch of it) "
                                 f"at M={ms_list[0]}"),
-                     "avg_us": kus, "bytes_per_launch": wbytes},
+                     "avg_us": lus, "bytes_per_launch": wbytes},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on layer 0 (bounded sample)")

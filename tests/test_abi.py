@@ -77,16 +77,33 @@ def test_gemm_misaligned(lib, buf):
         assert lib.nvfp4_gemm(x, wq, ws, 1.0, 1, 16, 16, p, None) == VG_ERR_ALIGN
 
 
-def test_gemm_ex_ignores_workspace(lib, buf):
+def test_gemm_ex_workspace_contract(lib, buf):
+    """nvfp4_gemm_ex slices a narrow matrix's blocks over more workgroups
+    when given the workspace vg_gemm_workspace_bytes asks for; a smaller
+    one is an error and a NULL one means no slicing (checked on the host,
+    before any launch)."""
     _, p = buf
-    assert lib.vg_gemm_workspace_bytes(17, 5120, 5120) == 0
+    need = lib.vg_gemm_workspace_bytes(17, 5120, 17408)
+    assert need > 0
+    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 17408, p, p, need - 1, None) == VG_ERR_WORKSPACE
+    assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 17408, p, p + 4, need, None) == VG_ERR_ALIGN
     # validation still applies to the _ex form
     assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 24, p, None, 0, None) == VG_ERR_SHAPE
 
 
 def test_workspace_sizes(lib):
-    for m, n, k in [(1, 5120, 5120), (17, 5120, 5120), (68, 5120, 17408), (0, 1, 16)]:
+    # M = 1 takes the GEMV kernel, K = 1024 is too short to slice, invalid shapes need nothing
+    for m, n, k in [(1, 5120, 5120), (17, 5120, 1024), (0, 1, 16), (69, 5120, 5120), (17, 5120, 24)]:
         assert lib.vg_gemm_workspace_bytes(m, n, k) == 0
+    # narrow matrices at M >= 2: 80 blocks of 64 rows, 3 K slices each; a
+    # counter area of one size for every shape, then an M x 64 float block
+    # per slice
+    sizes = {}
+    for m, n, k in [(17, 5120, 5120), (68, 5120, 17408), (2, 5120, 17408)]:
+        sizes[m] = lib.vg_gemm_workspace_bytes(m, n, k)
+        assert sizes[m] > 240 * m * 64 * 4
+    counters = {b - 240 * m * 64 * 4 for m, b in sizes.items()}
+    assert len(counters) == 1 and counters.pop() % 256 == 0
     assert lib.vg_lmhead_workspace_bytes(17) >= 8 * 68 * 16
     assert lib.vg_lmhead_workspace_bytes(0) == 0 and lib.vg_lmhead_workspace_bytes(69) == 0
 

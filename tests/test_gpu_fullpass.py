@@ -29,7 +29,7 @@ def host_bits(x):
 def test_full_step_sampled(weights, M):
     print(f"[case] full step M={M}", flush=True)
     run = weightpass.PassRun(weights, M)
-    run.run()
+    run.run_persistent()
     torch.cuda.synchronize()
     assert run.check() == 0
     rng = np.random.default_rng(40000 + M)
@@ -69,7 +69,7 @@ def test_full_step_lmhead_argmax_accept(weights):
     drafts = synth.gen_drafts(np.random.default_rng(41000), ref["argmax"].reshape(1, M), synth.VOCAB)
     run.set_drafts(torch.from_numpy(drafts).cuda())
     ref = oracle.lmhead_ref(x, wq, ws, lm["g"], T=M, drafts=drafts)
-    run.run()
+    run.run_persistent()
     torch.cuda.synchronize()
     assert run.check() == 0
     am = run.argmax.cpu().numpy()
@@ -97,8 +97,8 @@ def test_fused_projections_full_size(weights, M):
     sep = weightpass.PassRun(weights, M)
     fus = weightpass.PassRun(weights, M, fused=True)
     assert fus.step.info()["jobs"] == 4 * weights.layers + 1
-    sep.run()
-    fus.run()
+    sep.run_persistent()
+    fus.run_persistent()
     torch.cuda.synchronize()
     assert sep.check() == 0 and fus.check() == 0
     for layer in range(weights.layers):

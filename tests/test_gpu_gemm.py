@@ -129,6 +129,31 @@ def test_bitwise_repeatable(m, n, k):
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("m,n,k", [(2, 5120, 17408), (17, 333, 5120), (68, 1000, 2048), (17, 5120, 5120)])
+def test_sliced_gemm_same_bits(m, n, k):
+    """With a workspace, nvfp4_gemm_ex deals a narrow matrix's K slices to
+    separate workgroups (the one completing a block adds the slice sums in
+    slice order); the bits equal nvfp4_gemm's, where one workgroup runs
+    every slice of a block, over three calls on one workspace (the counters
+    reset themselves), and stay within the oracle's bound."""
+    print(f"[case] sliced gemm M={m} N={n} K={k}", flush=True)
+    need = binding.gemm_workspace_bytes(m, n, k)
+    assert need > 0
+    rng = np.random.default_rng(9400 + m + n)
+    wq, ws = synth.gen_weights(rng, n, k)
+    x = synth.gen_x(rng, m, k)
+    xd, wqd, wsd = dev_bf16(x), dev_u8(wq), dev_u8(ws)
+    plain = binding.nvfp4_gemm(xd, wqd, wsd, 0.75).cpu().numpy()
+    ws_t = binding.new_workspace(need)
+    for _ in range(3):
+        y = binding.nvfp4_gemm(xd, wqd, wsd, 0.75, workspace=ws_t).cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), plain.view(np.uint32))
+    assert int(ws_t[:1024].count_nonzero()) == 0
+    y_ref, bound = oracle.nvfp4_gemm_ref(x, wq, ws, 0.75)
+    ok, worst, at = within_bound(y, y_ref, bound)
+    assert ok, f"worst err/bound {worst:.3g} at {at}"
+
+
 def test_workspace_reused_across_shapes():
     """One caller workspace serves shapes with different tile counts in turn:
     the split-K counters of one shape must never sit under another shape's

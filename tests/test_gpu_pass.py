@@ -94,14 +94,14 @@ def test_one_layer_step(M, T):
     p, host, ys, lm, lmhost = build(M, T, LAYER, (20000, 5120), 31000 + M)
     info = p.info()
     assert info["jobs"] == 8 and info["stages"] == 5
-    p.run()
+    p.run_persistent()
     torch.cuda.synchronize()
     assert p.check() == 0
     check_outputs(M, T, host, ys, lm, lmhost, f"M={M}")
     first = snapshot(ys, lm)
     # repeated launches: the control block resets itself
     for _ in range(3):
-        p.run()
+        p.run_persistent()
     torch.cuda.synchronize()
     assert p.check() == 0
     assert same(first, snapshot(ys, lm))
@@ -110,6 +110,26 @@ def test_one_layer_step(M, T):
         y.fill_(float("nan"))
     p.run_unfused()
     torch.cuda.synchronize()
+    assert same(first, snapshot(ys, lm))
+    p.close()
+
+
+@pytest.mark.parametrize("M,T", [(1, 1), (4, 1), (17, 17), (68, 17)])
+def test_default_schedule_same_bits(M, T):
+    """vg_pass_run takes the persistent launch at M = 1 and one launch per
+    job (narrow matrices sliced) above: the same bits as the persistent
+    launch at every M."""
+    print(f"[case] default schedule M={M}", flush=True)
+    p, host, ys, lm, lmhost = build(M, T, LAYER, (20000, 5120), 36000 + M)
+    p.run_persistent()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    first = snapshot(ys, lm)
+    for y in ys:
+        y.fill_(float("nan"))
+    p.run()
+    torch.cuda.synchronize()
+    assert p.check() == 0
     assert same(first, snapshot(ys, lm))
     p.close()
 
@@ -155,13 +175,13 @@ def test_spread_slices(M):
     assert grid >= torch.cuda.get_device_properties(0).multi_processor_count
     want = sum(sliced_items(-(-n // 64), k, grid) for n, k, _ in SPREAD) + sliced_items(-(-1000 // 64), 2048, grid)
     assert info["items"] == want
-    p.run()
+    p.run_persistent()
     torch.cuda.synchronize()
     assert p.check() == 0
     check_outputs(M, 1, host, ys, lm, lmhost, f"spread M={M}")
     first = snapshot(ys, lm)
     for _ in range(3):
-        p.run()
+        p.run_persistent()
     torch.cuda.synchronize()
     assert p.check() == 0
     assert same(first, snapshot(ys, lm))
@@ -180,7 +200,7 @@ ODD = [(77, 48, 0), (300, 1040, 0), (1, 2048, 1), (129, 272, 2), (64, 1024, 2), 
 def test_odd_shapes_step(M, T):
     print(f"[case] odd-shape step M={M} T={T}", flush=True)
     p, host, ys, lm, lmhost = build(M, T, ODD, (1000, 2048), 32000 + M)
-    p.run()
+    p.run_persistent()
     torch.cuda.synchronize()
     assert p.check() == 0
     check_outputs(M, T, host, ys, lm, lmhost, f"odd M={M}")
@@ -194,32 +214,36 @@ def test_odd_shapes_step(M, T):
 @pytest.mark.parametrize("M", [1, 17])
 def test_step_without_lmhead_and_lmhead_only(M):
     p, host, ys, lm, lmhost = build(M, 1, LAYER[:4], None, 33000 + M)
-    p.run()
+    p.run_persistent()
     torch.cuda.synchronize()
     check_outputs(M, 1, host, ys, None, None, "no lm_head")
     p.close()
     T = M
     p, host, ys, lm, lmhost = build(M, T, [], (70000, 5120), 34000 + M)
-    p.run()
+    p.run_persistent()
     torch.cuda.synchronize()
     assert p.check() == 0
     check_outputs(M, T, host, ys, lm, lmhost, "lm_head only")
     p.close()
 
 
-@pytest.mark.parametrize("M,T", [(1, 1), (17, 17)])
-def test_step_graph_replay(M, T):
-    """The single launch captured in a graph and replayed, with eager work
-    and synchronisation between replays: every replay equals the eager run."""
+@pytest.mark.parametrize("M,T,sched", [(1, 1, "run_persistent"), (17, 17, "run_persistent"), (17, 17, "run"),
+                                       (68, 17, "run")])
+def test_step_graph_replay(M, T, sched):
+    """The step (one persistent launch, or the default schedule: one launch
+    per job at M >= 2, narrow matrices sliced) captured in a graph and
+    replayed, with eager work and synchronisation between replays: every
+    replay equals the eager run."""
+    print(f"[case] graph replay M={M} {sched}", flush=True)
     p, host, ys, lm, lmhost = build(M, T, LAYER[:4], (9000, 5120), 35000 + M)
-    p.run()
+    getattr(p, sched)()
     torch.cuda.synchronize()
     eager = snapshot(ys, lm)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            p.run()
+            getattr(p, sched)()
     torch.cuda.synchronize()
     for rep in range(4):
         for y in ys:

@@ -177,7 +177,7 @@ def test_pass_batch_invariant_rows_and_tree():
 
     p17, ys17, lm17, host, _ = build_pass(17, 17, x17, np.random.default_rng(seed_w), v, INV,
                                           (tokens, parents), token_map)
-    p17.run()
+    p17.run_persistent()
     torch.cuda.synchronize()
     assert p17.check() == 0
     am, al, an = (t.cpu().numpy() for t in lm17)
@@ -197,7 +197,7 @@ def test_pass_batch_invariant_rows_and_tree():
     # row 0 alone, as an M = 1 batch-invariant pass: the same bits as in the 17-row pass
     x1 = {k: v_[:1].copy() for k, v_ in x17.items()}
     p1, ys1, lm1, _, _ = build_pass(1, 1, x1, np.random.default_rng(seed_w), v, INV, None, token_map)
-    p1.run()
+    p1.run_persistent()
     torch.cuda.synchronize()
     assert p1.check() == 0
     for y1, y17 in zip(ys1, ys17):
@@ -228,7 +228,7 @@ def test_row_scales_stack_matrices_bitwise(M):
         yf = torch.empty((M, 512), device="cuda")
         sep = binding.Pass([(x, wq[:304], ws[:304], gs[0], ya, 0), (x, wq[304:], ws[304:], gs[1], yb, 0)], M)
         fus = binding.Pass([(x, wq, ws, 123.0, yf, 0, rs)], M)   # gscale ignored with row scales
-        for run in ("run", "run_unfused"):
+        for run in ("run", "run_persistent", "run_unfused"):
             yf.fill_(float("nan"))
             getattr(sep, run)()
             getattr(fus, run)()

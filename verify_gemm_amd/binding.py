@@ -59,6 +59,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "vg_pass_check": (i32, [vp, ctypes.POINTER(i32)]),
         "vg_pass_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "vg_pass_grid": (i32, [vp, ctypes.POINTER(i32)]),
+        "vg_pass_run_persistent": (i32, [vp, vp]),
         "vg_pass_destroy": (None, [vp]),
         "nvfp4_gemm_invariant": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp]),
         "lmhead_verify": (i32, [vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -155,7 +156,8 @@ def nvfp4_gemm(x, wq, ws, gscale: float, y=None, *, workspace=None, invariant=Fa
     """Y[M][N] = gscale * X . dequant(Wq, Ws)^T (fp32).  x: bf16 [M][K];
     wq: uint8 [N][K/2]; ws: uint8 [N][K/16].  With ``workspace`` (a zeroed
     uint8 device tensor of gemm_workspace_bytes bytes) the _ex entry point
-    is used, otherwise the library-owned workspace.  ``invariant`` selects
+    is used, which slices narrow matrices over more workgroups (same bits).
+    ``invariant`` selects
     nvfp4_gemm_invariant (rows bit-identical for any M)."""
     torch = _torch()
     lib = load()
@@ -401,6 +403,9 @@ class Pass:
 
     def run_unfused(self, stream=None):
         _check(self._lib.vg_pass_run_unfused(self.handle, _stream_ptr(stream)), "vg_pass_run_unfused")
+
+    def run_persistent(self, stream=None):
+        _check(self._lib.vg_pass_run_persistent(self.handle, _stream_ptr(stream)), "vg_pass_run_persistent")
 
     def check(self) -> int:
         e = ctypes.c_int(0)

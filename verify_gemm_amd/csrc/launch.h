@@ -109,6 +109,8 @@ int stream_rows_per_item(int M, int K, bool invariant, int fmt);
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream);
 // The exact grid a STATIC launch of a batch of M rows uses (all resident).
 int stream_static_grid(int M, bool invariant);
+// An upper bound of stream_static_grid over every M on this device.
+int stream_max_grid();
 
 // M = 1: the whole step (or a single GEMM / lm_head) as one launch of
 // step_gemv_grid() resident workgroups; rows of every job split evenly.

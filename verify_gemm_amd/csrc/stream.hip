@@ -1068,9 +1068,9 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2
   __shared__ int lds_dep[VG_MAX_M_DEV];
   if constexpr (MODE == MODE_DIRECT) {
     auto nodep = [] { return true; };
-    const SpreadCtx nosp{nullptr, nullptr, nullptr};
+    const SpreadCtx dsp{a.part, a.part_cnt, &lds_flag};
     NoBest nobest;
-    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, nosp, nobest);
+    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, dsp, nobest);
     return;
   } else {
     StreamCtl* ctl = a.ctl;
@@ -1230,6 +1230,8 @@ int stream_static_grid(int M, bool invariant) {
   const int want = (stream_mt_class(M, invariant) == 2 ? 2 : 1) * num_cus();
   return cap < want ? cap : want;
 }
+
+int stream_max_grid() { return 2 * num_cus(); }
 
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
   switch (stream_mt_class(a.M, a.invariant != 0)) {

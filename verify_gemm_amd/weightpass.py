@@ -141,6 +141,9 @@ class PassRun:
     def run_unfused(self, stream=None):
         self.step.run_unfused(stream)
 
+    def run_persistent(self, stream=None):
+        self.step.run_persistent(stream)
+
     def capture_unfused(self) -> torch.cuda.CUDAGraph:
         """The one-launch-per-matrix schedule captured into a graph."""
         self.run_unfused()
