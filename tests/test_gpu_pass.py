@@ -140,8 +140,8 @@ SPREAD = [(1280, 17408, 0), (333, 5120, 1), (4096, 1024, 2), (16640, 5120, 3)]
 def sliced_items(blocks, k, grid):
     """Items of a one-job stage of `blocks` 64-row blocks under the step's
     slicing rule: S = clamp(W // 4, 1, 3) slices of the W = ceil(K/256)
-    windows; all blocks sliced when fewer than the grid and estimated faster,
-    else the blocks past the last whole round."""
+    windows; all blocks sliced when fewer than the compute units (`grid`)
+    and estimated faster, else the blocks past the last whole round."""
     w = -(-k // 256)
     s = min(3, max(1, w // 4))
     whole = -(-blocks // grid) * w
@@ -171,9 +171,9 @@ def test_spread_slices(M):
     print(f"[case] spread slices M={M}", flush=True)
     p, host, ys, lm, lmhost = build(M, 1, SPREAD, (1000, 2048), 33000 + M)
     info = p.info()
-    grid = info["grid"]
-    assert grid >= torch.cuda.get_device_properties(0).multi_processor_count
-    want = sum(sliced_items(-(-n // 64), k, grid) for n, k, _ in SPREAD) + sliced_items(-(-1000 // 64), 2048, grid)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert info["grid"] >= cus
+    want = sum(sliced_items(-(-n // 64), k, cus) for n, k, _ in SPREAD) + sliced_items(-(-1000 // 64), 2048, cus)
     assert info["items"] == want
     p.run_persistent()
     torch.cuda.synchronize()

@@ -111,6 +111,9 @@ hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t st
 int stream_static_grid(int M, bool invariant);
 // An upper bound of stream_static_grid over every M on this device.
 int stream_max_grid();
+// Compute units of the current device (what several resident workgroups of
+// one CU share: its memory bandwidth).
+int stream_num_cus();
 
 // M = 1: the whole step (or a single GEMM / lm_head) as one launch of
 // step_gemv_grid() resident workgroups; rows of every job split evenly.

@@ -422,6 +422,10 @@ struct MfmaLdsItem {
     }
   }
 
+  // The activation fragments of MFMA step st+1 are read from LDS while
+  // step st multiplies (two register sets): with the reads of a step issued
+  // only after the previous step's MFMAs, every step waited one LDS round
+  // trip, and with one wave per SIMD nothing else hid it.
   __device__ __forceinline__ void window(int p, const unsigned char* slot) {
     const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
     f32x2 s[NT][2];
@@ -430,20 +434,25 @@ struct MfmaLdsItem {
       s[nt][0] = e4m3x2_lo((unsigned short)(sc[p][nt] & 0xFFFFu));
       s[nt][1] = e4m3x2_lo((unsigned short)(sc[p][nt] >> 16));
     }
+    u32x4 a[2][MT];
+    auto read = [&](int st, u32x4 (&dst)[MT]) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        dst[mt] = *reinterpret_cast<const u32x4*>(slot + 512 * (16 * mt + c) + 16 * ((8 * gq + st) ^ c));
+    };
+    read(0, a[0]);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) read(st + 1, a[(st + 1) & 1]);
       bf16x8 b[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) b[nt] = dequant8_bf16(q[p][nt][st >> 2][st & 3], s[nt][st >> 2][(st >> 1) & 1]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + c;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(slot + 512 * m + 16 * ((8 * gq + st) ^ c));
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b[nt],
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[st & 1][mt]), b[nt],
                                                                 acc[mt][nt], 0, 0, 0);
-      }
     }
   }
 
@@ -1232,6 +1241,7 @@ int stream_static_grid(int M, bool invariant) {
 }
 
 int stream_max_grid() { return 2 * num_cus(); }
+int stream_num_cus() { return num_cus(); }
 
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
   switch (stream_mt_class(a.M, a.invariant != 0)) {
