@@ -471,26 +471,19 @@ struct MfmaLdsItem {
       }
     store_x(0, lds);
     // The loop over whole groups of P windows must be entered in the order
-    // its own iterations leave the loads in, and contain no skipped step:
+    // its own iterations leave the loads in, and contain no skipped load:
     // a loop header reached with another order (the first P windows' loads
     // went out as all weights before the stage wait, then all activations)
-    // or with fewer loads (a skipped step) gets the compiler's most
-    // conservative wait -- all loads -- in every iteration.  So the first
-    // group is peeled off, the loop runs whole groups only, and the last,
-    // partial group (or all of a short K) is done step by step.
-    int base = 0;
-    if (cnt >= 2 * P) {
+    // or with fewer loads gets the compiler's most conservative wait -- all
+    // loads -- in every iteration.  So the first group is peeled off and
+    // every group is whole: steps past the item's last window still issue
+    // their (out-of-range, zero-traffic) loads and skip only the compute.
+    const int groups = (cnt + P - 1) / P;
 #pragma unroll
-      for (int p = 0; p < P; ++p) step(p, p, lds);
-      for (base = P; base + P <= cnt; base += P) {
+    for (int p = 0; p < P; ++p) step(p, p, lds);
+    for (int g = 1; g < groups; ++g) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) step(p, base + p, lds);
-      }
-    }
-    for (; base < cnt; base += P) {
-#pragma unroll
-      for (int p = 0; p < P; ++p)
-        if (base + p < cnt) step(p, base + p, lds);
+      for (int p = 0; p < P; ++p) step(p, g * P + p, lds);
     }
     if (fold_at >= 0) {
 #pragma unroll
@@ -520,8 +513,10 @@ struct MfmaLdsItem {
   // v0 + i + P into position p.
   __device__ __forceinline__ void step(int p, int i, unsigned char* lds) {
     __syncthreads();  // window i is in LDS; every wave is done with window i-1
-    window(p, lds + (i & 1) * kSlotBytes);
-    if (v0 + i + 1 == fold_at) fold();
+    if (i < cnt) {    // wave-uniform; nothing in here loads from memory
+      window(p, lds + (i & 1) * kSlotBytes);
+      if (v0 + i + 1 == fold_at) fold();
+    }
     store_x(p + 1 < P ? p + 1 : 0, lds + ((i + 1) & 1) * kSlotBytes);
     load_x(p, v0 + i + P);
     load_w(p, v0 + i + P);
