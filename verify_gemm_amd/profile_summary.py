@@ -64,10 +64,17 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
             continue
         lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    lines += ["", "Each kernel launch is one whole pass: step_gemv_kernel at M = 1; stream_kernel<MT, 2> "
-              "(MT 16-row M-tiles, static schedule) at M >= 2 -- <2, 2> at M = 17, <5, 2> at M = 68.", ""]
+    lines += ["", "A launch of step_gemv_kernel (M = 1) or of stream_kernel<MT, 2> (MT 16-row M-tiles: <2, 2> "
+              "at M = 17, <5, 2> at M = 68; the persistent schedule) is one whole pass.  At M >= 2 the "
+              f"step's default schedule is one launch per job: {GEMM_JOBS_PER_PASS} GEMM launches of "
+              "stream_kernel<MT, 0> and one lm_head launch of stream_kernel<MT, 1> per pass.", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
+
+
+# The timed step (257 jobs): 64 layers x {q|k|v, o, gate|up, down} GEMMs,
+# then the lm_head.
+GEMM_JOBS_PER_PASS = 256
 
 
 # The fill kernel of known size is one of many torch fills in a run (small
@@ -110,7 +117,16 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
               "Traffic per launch (scaled fetch + scaled write) against the pass's algorithmic "
               f"{PASS_WEIGHT_BYTES} weight bytes:", ""]
     for k, v in traffic.items():
-        lines.append(f"* {k}: {v} bytes ({v / PASS_WEIGHT_BYTES:.3f}x)")
+        if k.endswith(", 2>") or k.startswith("step_gemv"):
+            lines.append(f"* {k}: {v} bytes ({v / PASS_WEIGHT_BYTES:.3f}x)")
+    # one launch per job: the GEMM launches of a pass (same mix every pass)
+    # plus its lm_head launch
+    for k, v in traffic.items():
+        if k.endswith(", 0>"):
+            lm = k[:-2] + "1>"
+            per_pass = v * GEMM_JOBS_PER_PASS + traffic.get(lm, 0)
+            lines.append(f"* {k} x {GEMM_JOBS_PER_PASS} + {lm} (one launch per job): {per_pass} bytes per pass "
+                         f"({per_pass / PASS_WEIGHT_BYTES:.3f}x)")
     record = {"sources_sha256": sources_hash(), "traffic_bytes": traffic,
               "fetch_scale": f_scale, "write_scale": w_scale}
     lines += ["", "Machine-readable record (bench.py reads it):", "", "```json", json.dumps(record, indent=1),
