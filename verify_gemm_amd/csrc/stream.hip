@@ -46,6 +46,8 @@
 //     target's own token replaces the first wrong guess) and zeroes the
 //     control block for the next launch -- no host memset, so a step can be
 //     replayed from a graph.
+#include <type_traits>
+
 #include "launch.h"
 #include "nvfp4_device.h"
 
@@ -330,13 +332,17 @@ struct MfmaItem {
 // q (elements 8q .. 8q+7 of the window) at position q ^ (m & 15), so that
 // the 16 lanes reading rows 16*mt + c, piece q, hit 16 different bank
 // groups (and the 32 lanes writing one row hit 32 different ones).
-template <int MT, int NT, int P>
+template <int MT, int NT, int P, int FMT = 0>
 struct MfmaLdsItem {
   static constexpr int kRows = 16 * NT * kWaves;
   static constexpr int kSlotBytes = 16 * MT * 512;
   static constexpr int kRing = 2;  // slots: the window being read, the next one being written
   static constexpr int kXLoads = 2 * MT;  // activation loads per lane per window
-  u32x4 q[P][NT][2];
+  // A lane's 64 weights of a window: NVFP4 32 code bytes + 4 scale bytes;
+  // FP8 (E4M3, scales per row in the epilogue) 64 bytes.
+  static constexpr int kQ = FMT == 0 ? 2 : 4;        // 16-byte weight loads per lane per window
+  static constexpr unsigned kLaneBytes = 16u * kQ;   // a lane's weight bytes per window
+  u32x4 q[P][NT][kQ];
   unsigned sc[P][NT];
   u32x4 xq[P][kXLoads];  // this wave's rows of the activation window, per ring position
   f32x4 acc[MT][NT];     // the running slice's sum; after compute(), the result (see fold)
@@ -354,10 +360,12 @@ struct MfmaLdsItem {
     const bool in = v < vend && 256u * (unsigned)v + ew < (unsigned)k;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const unsigned o = cw + 128u * (unsigned)v;
-      q[p][nt][0] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? o : kOOB, 0, 0);
-      q[p][nt][1] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? o + 16u : kOOB, 0, 0);
-      sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b32(rs[nt], in ? cs + 16u * (unsigned)v : kOOB, 0, 0);
+      const unsigned o = cw + 4u * kLaneBytes * (unsigned)v;
+#pragma unroll
+      for (int t = 0; t < kQ; ++t)
+        q[p][nt][t] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? o + 16u * t : kOOB, 0, 0);
+      if constexpr (FMT == 0)
+        sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b32(rs[nt], in ? cs + 16u * (unsigned)v : kOOB, 0, 0);
     }
   }
 
@@ -366,7 +374,7 @@ struct MfmaLdsItem {
   __device__ __forceinline__ void issue(const StreamJob& j, int block, int slice) {
     const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const unsigned rb = (unsigned)j.k >> 1, sb = (unsigned)j.k >> 4;
+    const unsigned rb = FMT == 0 ? (unsigned)j.k >> 1 : (unsigned)j.k, sb = (unsigned)j.k >> 4;
     n0 = block * kRows;
     k = j.k;
     nw = lds_windows(j.k);
@@ -388,9 +396,9 @@ struct MfmaLdsItem {
       const int t0 = n0 + 16 * (NT * w + nt);
       const int rows = j.n - t0 < 0 ? 0 : (j.n - t0 > 16 ? 16 : j.n - t0);
       rw[nt] = rsrc_uniform(j.wq + (size_t)t0 * rb, (unsigned)rows * rb);
-      rs[nt] = rsrc_uniform(j.ws + (size_t)t0 * sb, (unsigned)rows * sb);
+      if constexpr (FMT == 0) rs[nt] = rsrc_uniform(j.ws + (size_t)t0 * sb, (unsigned)rows * sb);
     }
-    cw = (unsigned)c * rb + 32u * (unsigned)gq;
+    cw = (unsigned)c * rb + kLaneBytes * (unsigned)gq;
     cs = (unsigned)c * sb + 4u * (unsigned)gq;
     ew = 64u * (unsigned)gq;
 #pragma unroll
@@ -429,10 +437,12 @@ struct MfmaLdsItem {
   __device__ __forceinline__ void window(int p, const unsigned char* slot) {
     const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
     f32x2 s[NT][2];
+    if constexpr (FMT == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      s[nt][0] = e4m3x2_lo((unsigned short)(sc[p][nt] & 0xFFFFu));
-      s[nt][1] = e4m3x2_lo((unsigned short)(sc[p][nt] >> 16));
+      for (int nt = 0; nt < NT; ++nt) {
+        s[nt][0] = e4m3x2_lo((unsigned short)(sc[p][nt] & 0xFFFFu));
+        s[nt][1] = e4m3x2_lo((unsigned short)(sc[p][nt] >> 16));
+      }
     }
     u32x4 a[2][MT];
     auto read = [&](int st, u32x4 (&dst)[MT]) {
@@ -446,7 +456,12 @@ struct MfmaLdsItem {
       if (st + 1 < 8) read(st + 1, a[(st + 1) & 1]);
       bf16x8 b[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[nt] = dequant8_bf16(q[p][nt][st >> 2][st & 3], s[nt][st >> 2][(st >> 1) & 1]);
+      for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (FMT == 0)
+          b[nt] = dequant8_bf16(q[p][nt][st >> 2][st & 3], s[nt][st >> 2][(st >> 1) & 1]);
+        else  // bytes 8st .. 8st+7 of the lane's 64: elements 64gq + 8st .. + 7, exact in bf16
+          b[nt] = fp8x8_bf16(q[p][nt][st >> 1][2 * (st & 1)], q[p][nt][st >> 1][2 * (st & 1) + 1]);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -752,6 +767,7 @@ struct Cfg {
   static constexpr int LNT = 1;
   static constexpr int LP = MT <= 2 ? 4 : 2;
   using Lds = MfmaLdsItem<MT, LNT, LP>;
+  using LdsF8 = MfmaLdsItem<MT, LNT, LP, 1>;  // FP8 weights, the same item otherwise
 };
 
 // Processes one item of job j.  `dep` is called by every thread after the
@@ -848,10 +864,10 @@ __device__ __forceinline__ float ld_agent_f(const float* p) {
 // itself in; the workgroup that completes the block adds the slice sums
 // from +0.0 in slice order -- as a whole-block item folds them -- and
 // finishes the rows, then clears the count for the next launch.
-template <int MT, class Dep, class BestT>
+template <int MT, int FMT, class Dep, class BestT>
 __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M, Dep&& dep, unsigned char* xring,
                                              const SpreadCtx& sp, BestT& best) {
-  using Item = typename Cfg<MT>::Lds;
+  using Item = std::conditional_t<FMT == 0, typename Cfg<MT>::Lds, typename Cfg<MT>::LdsF8>;
   constexpr int NT = Cfg<MT>::LNT, R = Item::kRows;
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4, w = threadIdx.x >> 6;
   const int S = lds_slices(j.k), first = j.spread - 1;
@@ -927,22 +943,28 @@ __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M
     }
 }
 
-template <int MT, class Dep, class BestT>
+// One item of job j, whose weight format is FMT (a launch holds one format:
+// each kernel carries only its own items, so one format's registers do not
+// crowd the other's).
+template <int MT, int FMT, class Dep, class BestT>
 __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, Dep&& dep, float* red,
                                          unsigned char* xring, const SpreadCtx& sp, BestT& best) {
   if constexpr (MT == 0) {
-    if (j.fmt == 1) gemv_generic_run<Fp8GemvItem>(j, item, dep, best);
-    else if (j.k == 5120) gemv_run<5, 4>(j, item, dep, best);
-    else if (j.k == 17408) gemv_run<17, 1>(j, item, dep, best);
-    else if (j.k == 1024) gemv_run<1, 8>(j, item, dep, best);
-    else gemv_generic_run<GemvGenericItem>(j, item, dep, best);
+    if constexpr (FMT == 1) {
+      gemv_generic_run<Fp8GemvItem>(j, item, dep, best);
+    } else {
+      if (j.k == 5120) gemv_run<5, 4>(j, item, dep, best);
+      else if (j.k == 17408) gemv_run<17, 1>(j, item, dep, best);
+      else if (j.k == 1024) gemv_run<1, 8>(j, item, dep, best);
+      else gemv_generic_run<GemvGenericItem>(j, item, dep, best);
+    }
   } else {
     constexpr int NT = Cfg<MT>::NT;
-    if (j.fmt == 1) {
+    if ((j.k & 127) == 0) {
+      mfma_lds_run<MT, FMT>(j, item, M, dep, xring, sp, best);
+    } else if constexpr (FMT == 1) {
       Fp8MfmaItem<MT, NT> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
-    } else if ((j.k & 127) == 0) {
-      mfma_lds_run<MT>(j, item, M, dep, xring, sp, best);
     } else {
       MfmaGuardedItem<MT, NT> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
@@ -1056,7 +1078,7 @@ __device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am, 
   if (tid == 0) st_agent(&ctl->exits, 0u);
 }
 
-template <int MT, int MODE>
+template <int MT, int MODE, int FMT>
 // Two M-tiles: registers capped for two waves per SIMD, so the step can
 // keep two workgroups per CU (measured: the M = 17 step 4 % faster; one
 // M-tile and three or more gain nothing or lose).
@@ -1074,7 +1096,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2
     auto nodep = [] { return true; };
     const SpreadCtx dsp{a.part, a.part_cnt, &lds_flag};
     NoBest nobest;
-    run_item<MT>(a.job0, blockIdx.x, a.M, nodep, red, xring, dsp, nobest);
+    run_item<MT, FMT>(a.job0, blockIdx.x, a.M, nodep, red, xring, dsp, nobest);
     return;
   } else {
     StreamCtl* ctl = a.ctl;
@@ -1120,7 +1142,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2
         }
         return true;
       };
-      run_item<MT>(j, item, a.M, dep, red, xring, sp, best);
+      run_item<MT, FMT>(j, item, a.M, dep, red, xring, sp, best);
       // LDS reuse by the next item (M >= 2: its activation copies go into
       // ring slots the slowest wave may still be reading)
       if constexpr (MODE == MODE_STATIC || MT > 0) __syncthreads();
@@ -1160,35 +1182,43 @@ int num_cus() {
   return cus;
 }
 
-template <int MT, int MODE>
+template <int MT, int MODE, int FMT = 0>
 int resident_blocks() {
   static int per_cu = 0;
   if (!per_cu) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<MT, MODE>, kWG, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<MT, MODE, FMT>, kWG, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
   return per_cu * num_cus();
 }
 
-template <int MT>
-hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
+template <int MT, int FMT>
+hipError_t launch_fmt(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
   switch (mode) {
     case MODE_DIRECT:
-      hipLaunchKernelGGL((stream_kernel<MT, MODE_DIRECT>), dim3(grid), dim3(kWG), 0, stream, a);
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_DIRECT, FMT>), dim3(grid), dim3(kWG), 0, stream, a);
       break;
     case MODE_GRID: {
-      const int cap = resident_blocks<MT, MODE_GRID>();
-      hipLaunchKernelGGL((stream_kernel<MT, MODE_GRID>), dim3(grid < cap ? grid : cap), dim3(kWG), 0, stream, a);
+      const int cap = resident_blocks<MT, MODE_GRID, FMT>();
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_GRID, FMT>), dim3(grid < cap ? grid : cap), dim3(kWG), 0, stream,
+                         a);
       break;
     }
     default:
       // exactly stream_static_grid(M) workgroups: the stage targets count them
-      hipLaunchKernelGGL((stream_kernel<MT, MODE_STATIC>), dim3(grid), dim3(kWG), 0, stream, a);
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_STATIC, FMT>), dim3(grid), dim3(kWG), 0, stream, a);
       break;
   }
   return hipGetLastError();
+}
+
+// The weight format of a launch is that of its (first) job: a step's jobs
+// are all NVFP4; FP8 comes only as single-job launches.
+template <int MT>
+hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
+  return a.job0.fmt == 1 ? launch_fmt<MT, 1>(a, mode, grid, stream) : launch_fmt<MT, 0>(a, mode, grid, stream);
 }
 
 }  // namespace
@@ -1214,7 +1244,7 @@ int stream_rows_per_item(int M, int K, bool invariant, int fmt) {
     if (K == 1024) return GemvItem<1, 8>::kRows;
     return GemvGenericItem::kRows;
   }
-  if (fmt == 0 && (K & 127) == 0) return stream_lds_rows(M, invariant);
+  if ((K & 127) == 0) return stream_lds_rows(M, invariant);  // the LDS-shared item, NVFP4 or FP8
   return 16 * (mt <= 2 ? 2 : 4);
 }
 
