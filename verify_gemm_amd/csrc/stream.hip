@@ -728,11 +728,56 @@ struct Best {
   __device__ __forceinline__ void offer(int r, float val, int idx) {
     if (i[r] < 0 || better(val, idx, v[r], i[r])) { v[r] = val; i[r] = idx; }
   }
+  __device__ __forceinline__ void begin_item() {}
+  __device__ __forceinline__ void end_item() {}
 };
 
 // Items of GEMM jobs keep no running best.
 struct NoBest {
   __device__ __forceinline__ void offer(int, float, int) {}
+  __device__ __forceinline__ void begin_item() {}
+  __device__ __forceinline__ void end_item() {}
+};
+
+// The lm_head's running best with M-tiles: kept in LDS, one key per row m
+// per wave, so nothing of it is live in registers across an item's window
+// loop.  An item's candidates (lane (c, gq) offers rows m = 16*mt + 4*gq + r
+// for its columns) collect in registers during the item's epilogue only;
+// end_item() reduces them over the 16 lanes that share each m (largest
+// logit, then lowest index: the larger packed key) and folds them into the
+// wave's table.
+template <int MT>
+struct WaveBest {
+  static constexpr int R = MT * 4;
+  unsigned long long* tab;  // this wave's 16 * MT keys (LDS); 0 = no candidate yet
+  float v[R];
+  int i[R];
+  __device__ __forceinline__ void init() {
+    for (int m = threadIdx.x & 63; m < 16 * MT; m += kWave) tab[m] = 0ull;  // 80 rows at MT = 5
+  }
+  __device__ __forceinline__ void begin_item() {
+#pragma unroll
+    for (int r = 0; r < R; ++r) { v[r] = -__builtin_inff(); i[r] = -1; }
+  }
+  __device__ __forceinline__ void offer(int r, float val, int idx) {
+    if (i[r] < 0 || better(val, idx, v[r], i[r])) { v[r] = val; i[r] = idx; }
+  }
+  __device__ __forceinline__ void end_item() {
+    const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        unsigned long long k = i[mt * 4 + r] >= 0 ? argmax_key(v[mt * 4 + r], (unsigned)i[mt * 4 + r]) : 0ull;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+          const unsigned long long o = __shfl_xor(k, off, kWave);
+          k = o > k ? o : k;
+        }
+        const int m = 16 * mt + 4 * gq + r;
+        if (c == 0 && k > tab[m]) tab[m] = k;
+      }
+  }
 };
 
 __device__ __forceinline__ void publish_best(StreamCtl* ctl, int m, float v, int idx) {
@@ -829,6 +874,7 @@ __device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item,
   reduce_waves<MT, NT>(it.acc, red, j.g);
   if (!ok || (threadIdx.x >> 6) != 0) return;
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  best.begin_item();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -845,6 +891,7 @@ __device__ __forceinline__ void mfma_run(Item& it, const StreamJob& j, int item,
         }
       }
     }
+  best.end_item();
 }
 
 // Where a spread job's slice sums meet (STATIC launches; null elsewhere).
@@ -926,6 +973,7 @@ __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M
     if (threadIdx.x == 0) st_agent(count, 0u);
   }
   if (!ok) return;
+  best.begin_item();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -941,6 +989,7 @@ __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M
         }
       }
     }
+  best.end_item();
 }
 
 // One item of job j, whose weight format is FMT (a launch holds one format:
@@ -987,22 +1036,14 @@ __device__ __forceinline__ void publish(StreamCtl* ctl, int M, BestT& best) {
     if (lane == 0) publish_best(ctl, 0, v, i);
   } else {
     (void)w;
-    const int c = lane & 15, gq = lane >> 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = best.v[mt * 4 + r];
-        int i = best.i[mt * 4 + r];
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-          const float ov = __shfl_xor(v, off, kWave);
-          const int oi = __shfl_xor(i, off, kWave);
-          if (oi >= 0 && (i < 0 || better(ov, oi, v, i))) { v = ov; i = oi; }
-        }
-        const int m = 16 * mt + 4 * gq + r;
-        if (c == 0 && m < M) publish_best(ctl, m, v, i);
-      }
+    // this wave's table: one key per row m (0: the wave saw none); more
+    // rows than lanes at MT = 5
+    for (int m = lane; m < 16 * MT && m < M; m += kWave) {
+      const unsigned long long k = best.tab[m];
+      if (k != 0ull)
+        __hip_atomic_fetch_max(&ctl->keys[m][blockIdx.x % kKeySlots], k, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1092,6 +1133,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2
   __shared__ int lds_flag;
   __shared__ int lds_am[VG_MAX_M_DEV];
   __shared__ int lds_dep[VG_MAX_M_DEV];
+  __shared__ unsigned long long lds_best[kWaves][MT == 0 ? 1 : 16 * MT];  // lm_head keys per wave and row
   if constexpr (MODE == MODE_DIRECT) {
     auto nodep = [] { return true; };
     const SpreadCtx dsp{a.part, a.part_cnt, &lds_flag};
@@ -1151,7 +1193,9 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2
       NoBest nobest;
       for (; t < lm_begin; t += G) body(t, nobest);
     }
-    Best<MT == 0 ? 1 : MT * 4> best;
+    using BestT = std::conditional_t<MT == 0, Best<1>, WaveBest<MT == 0 ? 1 : MT>>;
+    BestT best;
+    if constexpr (MT > 0) best.tab = &lds_best[threadIdx.x >> 6][0];
     best.init();
     for (; t < a.total_items; t += G) body(t, best);
     if constexpr (MODE == MODE_STATIC) {
