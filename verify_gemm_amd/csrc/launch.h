@@ -90,6 +90,7 @@ struct StreamArgs {
   int32_t* accept_node;          // [M/T] node whose argmax is the bonus token, or null
   int lm_rows;                   // V of the lm_head job (bounds the token_map lookup)
   int invariant;                 // 1: every M on the MFMA path (row results independent of M)
+  int any_k;                     // a job list (jobs != nullptr) with a K that is not a multiple of 128
   float* part;                   // spread jobs: [slot][M][64] slice sums of a block
   unsigned* part_cnt;            // spread jobs: [slot] slices done of the block whose slice 0 is that slot
 };

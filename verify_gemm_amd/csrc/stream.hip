@@ -994,8 +994,10 @@ __device__ __forceinline__ void mfma_lds_run(const StreamJob& j, int item, int M
 
 // One item of job j, whose weight format is FMT (a launch holds one format:
 // each kernel carries only its own items, so one format's registers do not
-// crowd the other's).
-template <int MT, int FMT, class Dep, class BestT>
+// crowd the other's).  ANYK = 0: every K of the launch is a multiple of 128,
+// so the kernel carries only the LDS-shared item (the K-split guarded items
+// are the register-heaviest code of the kernel).
+template <int MT, int FMT, int ANYK, class Dep, class BestT>
 __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, Dep&& dep, float* red,
                                          unsigned char* xring, const SpreadCtx& sp, BestT& best) {
   if constexpr (MT == 0) {
@@ -1009,8 +1011,9 @@ __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, De
     }
   } else {
     constexpr int NT = Cfg<MT>::NT;
-    if ((j.k & 127) == 0) {
+    if (!ANYK || (j.k & 127) == 0) {
       mfma_lds_run<MT, FMT>(j, item, M, dep, xring, sp, best);
+    } else if constexpr (!ANYK) {
     } else if constexpr (FMT == 1) {
       Fp8MfmaItem<MT, NT> it;
       mfma_run<MT, NT>(it, j, item, M, dep, red, best);
@@ -1119,7 +1122,7 @@ __device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am, 
   if (tid == 0) st_agent(&ctl->exits, 0u);
 }
 
-template <int MT, int MODE, int FMT>
+template <int MT, int MODE, int FMT, int ANYK>
 // Two M-tiles: registers capped for two waves per SIMD, so the step can
 // keep two workgroups per CU (measured: the M = 17 step 4 % faster; one
 // M-tile and three or more gain nothing or lose).
@@ -1138,7 +1141,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2
     auto nodep = [] { return true; };
     const SpreadCtx dsp{a.part, a.part_cnt, &lds_flag};
     NoBest nobest;
-    run_item<MT, FMT>(a.job0, blockIdx.x, a.M, nodep, red, xring, dsp, nobest);
+    run_item<MT, FMT, ANYK>(a.job0, blockIdx.x, a.M, nodep, red, xring, dsp, nobest);
     return;
   } else {
     StreamCtl* ctl = a.ctl;
@@ -1184,7 +1187,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2
         }
         return true;
       };
-      run_item<MT, FMT>(j, item, a.M, dep, red, xring, sp, best);
+      run_item<MT, FMT, ANYK>(j, item, a.M, dep, red, xring, sp, best);
       // LDS reuse by the next item (M >= 2: its activation copies go into
       // ring slots the slowest wave may still be reading)
       if constexpr (MODE == MODE_STATIC || MT > 0) __syncthreads();
@@ -1226,43 +1229,49 @@ int num_cus() {
   return cus;
 }
 
-template <int MT, int MODE, int FMT = 0>
+template <int MT, int MODE, int FMT = 0, int ANYK = 1>
 int resident_blocks() {
   static int per_cu = 0;
   if (!per_cu) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<MT, MODE, FMT>, kWG, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_kernel<MT, MODE, FMT, ANYK>, kWG, 0) != hipSuccess ||
+        n < 1)
       n = 1;
     per_cu = n;
   }
   return per_cu * num_cus();
 }
 
-template <int MT, int FMT>
+template <int MT, int FMT, int ANYK>
 hipError_t launch_fmt(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
   switch (mode) {
     case MODE_DIRECT:
-      hipLaunchKernelGGL((stream_kernel<MT, MODE_DIRECT, FMT>), dim3(grid), dim3(kWG), 0, stream, a);
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_DIRECT, FMT, ANYK>), dim3(grid), dim3(kWG), 0, stream, a);
       break;
     case MODE_GRID: {
-      const int cap = resident_blocks<MT, MODE_GRID, FMT>();
-      hipLaunchKernelGGL((stream_kernel<MT, MODE_GRID, FMT>), dim3(grid < cap ? grid : cap), dim3(kWG), 0, stream,
-                         a);
+      const int cap = resident_blocks<MT, MODE_GRID, FMT, ANYK>();
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_GRID, FMT, ANYK>), dim3(grid < cap ? grid : cap), dim3(kWG), 0,
+                         stream, a);
       break;
     }
     default:
       // exactly stream_static_grid(M) workgroups: the stage targets count them
-      hipLaunchKernelGGL((stream_kernel<MT, MODE_STATIC, FMT>), dim3(grid), dim3(kWG), 0, stream, a);
+      hipLaunchKernelGGL((stream_kernel<MT, MODE_STATIC, FMT, ANYK>), dim3(grid), dim3(kWG), 0, stream, a);
       break;
   }
   return hipGetLastError();
 }
 
 // The weight format of a launch is that of its (first) job: a step's jobs
-// are all NVFP4; FP8 comes only as single-job launches.
+// are all NVFP4; FP8 comes only as single-job launches.  A launch whose
+// every K is a multiple of 128 takes the kernel without the guarded items
+// (the GEMV kernels of MT = 0 have no such split).
 template <int MT>
 hipError_t launch_mt(const StreamArgs& a, int mode, int grid, hipStream_t stream) {
-  return a.job0.fmt == 1 ? launch_fmt<MT, 1>(a, mode, grid, stream) : launch_fmt<MT, 0>(a, mode, grid, stream);
+  const bool any_k = MT == 0 || (a.jobs ? a.any_k != 0 : (a.job0.k & 127) != 0);
+  if (a.job0.fmt == 1)
+    return any_k ? launch_fmt<MT, 1, 1>(a, mode, grid, stream) : launch_fmt<MT, 1, 0>(a, mode, grid, stream);
+  return any_k ? launch_fmt<MT, 0, 1>(a, mode, grid, stream) : launch_fmt<MT, 0, 0>(a, mode, grid, stream);
 }
 
 }  // namespace
