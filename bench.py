@@ -56,10 +56,11 @@ def parse():
 
 
 def step_kernel_name(M: int) -> str:
-    """The kernel one step launch runs: the M = 1 step kernel, else the
-    static-schedule stream kernel (every job of the pass has K % 64 == 0
-    and K <= 18432, so M = 1 always takes the step kernel)."""
-    return "step_gemv_kernel" if M == 1 else f"stream_kernel<{(M + 15) // 16}, 2>"
+    """The kernel one persistent step launch runs: the M = 1 step kernel,
+    else the static-schedule stream kernel <MT, MODE 2, NVFP4, every K a
+    multiple of 128> (every job of the pass has K % 64 == 0 and K <= 18432,
+    so M = 1 always takes the step kernel)."""
+    return "step_gemv_kernel" if M == 1 else f"stream_kernel<{(M + 15) // 16}, 2, 0, 0>"
 
 
 def log(msg):

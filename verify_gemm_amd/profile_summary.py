@@ -40,6 +40,13 @@ def sources_hash() -> str:
     return h.hexdigest()
 
 
+def stream_args(name: str):
+    """(MT, MODE, ...) of a stream_kernel<...> short name, or None."""
+    if not name.startswith("stream_kernel<"):
+        return None
+    return tuple(int(v) for v in name[len("stream_kernel<"):-1].split(","))
+
+
 def short_name(name: str) -> str | None:
     if "step_gemv_kernel" in name:
         return "step_gemv_kernel"
@@ -64,10 +71,11 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
             continue
         lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    lines += ["", "A launch of step_gemv_kernel (M = 1) or of stream_kernel<MT, 2> (MT 16-row M-tiles: <2, 2> "
-              "at M = 17, <5, 2> at M = 68; the persistent schedule) is one whole pass.  At M >= 2 the "
-              f"step's default schedule is one launch per job: {GEMM_JOBS_PER_PASS} GEMM launches of "
-              "stream_kernel<MT, 0> and one lm_head launch of stream_kernel<MT, 1> per pass.", ""]
+    lines += ["", "stream_kernel<MT, MODE, FMT, ANYK>: MT 16-row M-tiles (2 at M = 17, 5 at M = 68), MODE 0 "
+              "one GEMM job, 1 the lm_head, 2 the whole pass as one persistent launch; FMT 0 NVFP4; ANYK 0 "
+              "when every K is a multiple of 128.  A launch of step_gemv_kernel (M = 1) or of a MODE 2 "
+              f"kernel is one whole pass.  At M >= 2 the step's default schedule is one launch per job: "
+              f"{GEMM_JOBS_PER_PASS} GEMM launches of MODE 0 and one lm_head launch of MODE 1 per pass.", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
 
@@ -116,14 +124,18 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
               "smaller fills of the same run are left out).", "",
               "Traffic per launch (scaled fetch + scaled write) against the pass's algorithmic "
               f"{PASS_WEIGHT_BYTES} weight bytes:", ""]
+    # stream_kernel<MT, MODE, FMT, ANYK>: MODE 2 is one persistent launch
+    # of the whole pass; MODE 0 the per-job GEMM launches, MODE 1 the lm_head
     for k, v in traffic.items():
-        if k.endswith(", 2>") or k.startswith("step_gemv"):
-            lines.append(f"* {k}: {v} bytes ({v / PASS_WEIGHT_BYTES:.3f}x)")
+        a = stream_args(k)
+        if k.startswith("step_gemv") or (a is not None and a[1] == 2):
+            lines.append(f"* {k} (one launch per pass): {v} bytes ({v / PASS_WEIGHT_BYTES:.3f}x)")
     # one launch per job: the GEMM launches of a pass (same mix every pass)
     # plus its lm_head launch
     for k, v in traffic.items():
-        if k.endswith(", 0>"):
-            lm = k[:-2] + "1>"
+        a = stream_args(k)
+        if a is not None and a[1] == 0:
+            lm = "stream_kernel<" + ", ".join(str(x) for x in (a[0], 1) + a[2:]) + ">"
             per_pass = v * GEMM_JOBS_PER_PASS + traffic.get(lm, 0)
             lines.append(f"* {k} x {GEMM_JOBS_PER_PASS} + {lm} (one launch per job): {per_pass} bytes per pass "
                          f"({per_pass / PASS_WEIGHT_BYTES:.3f}x)")
