@@ -1,51 +1,53 @@
-// The NVFP4 weight-streaming kernels: one code path for a single GEMM, the
-// lm_head verify pass, and the whole decode / verify step.
+// The weight-streaming kernels for batches of M >= 2 rows (and M = 1 shapes
+// or formats the step kernel does not take): a single GEMM, the lm_head
+// verify pass, and a whole decode / verify step as one persistent launch.
 //
 // A step of the ~27B hybrid reads every weight once and is bound by memory
 // bandwidth (ling-engine README, opening paragraph and "Six levers";
-// veloGB10 docs, "Engineered to the roofline").  Measured on MI355X, a
-// workgroup that streams one contiguous region sustains a higher read rate
-// than a grid-stride walk, and every kernel launch costs a few microseconds
-// of ramp-up and drain -- as long as streaming a whole 5120x5120 NVFP4
-// matrix.  So the unit of work here is an ITEM: a contiguous block of
-// weight rows (all of K) handled by one 256-thread workgroup, and a step is
-// one persistent launch that streams items back to back:
+// veloGB10 docs, "Engineered to the roofline").  The unit of work is an
+// ITEM: a block of 64 weight rows -- or one K slice of such a block -- run
+// by one 256-thread workgroup.  Three launch modes:
 //
-//   * the step's items are numbered in pass order and dealt round-robin to
-//     a grid of co-resident workgroups (item i to workgroup i mod G), each
-//     working through its items in increasing order.  An item of stage s
-//     (the per-layer order {q,k,v} -> o -> {gate,up} -> down -> ... ->
-//     lm_head) may only consume its activations once stage s-1 is done; a
-//     workgroup issues the item's weight loads FIRST (weights never depend
-//     on activations) and only then waits, so HBM keeps streaming across the
-//     dependency.  Completion is signalled once per workgroup and stage, on
-//     one of eight counters per stage: measured, device-scope atomics on a
-//     single address serialise at several ns each, and a counter per item
-//     plus a ticket per item cost milliseconds per step.  Every workgroup
-//     only waits on stages whose items all precede its own in its order, so
-//     with all workgroups resident the waits cannot deadlock; they are
-//     bounded anyway and raise an error flag instead of hanging;
-//   * M = 1 (plain decode): each half-wave owns a weight row, lane L reads
-//     16-byte chunks L, L+32, ... (512 contiguous bytes per half-wave and
-//     instruction, nontemporal); per 16-block eight v_dot2_f32_bf16 multiply
-//     the unscaled E2M1 values (exact in bf16) with X and one FMA applies
-//     the E4M3 block scale (~1.1 VALU ops per weight element);
-//   * M >= 2 (verify, 17 or 68 rows): v_mfma_f32_16x16x32_bf16 on weights
-//     dequantised exactly to bf16 (E4M3 x E2M1 has <= 6 significant bits);
-//     an item is 16*NT weight rows, the four waves take a quarter of K
-//     each, stream their windows through a register ring of P 128-element
-//     windows, and meet in LDS where the four partial tiles are added in a
-//     fixed order -- no global partial sums and no float atomics, so every
-//     result is bitwise repeatable;
-//   * the lm_head never writes logits: each workgroup keeps the best
-//     (logit, lowest index) per row across its items and publishes it once
-//     as a 64-bit key with an unsigned atomic max into one of 16 slots per
-//     row (spreading the atomics); the last workgroup to leave reads the
-//     slots, writes argmax, runs the greedy accept rule per sequence
-//     (TandemLLM README, introduction: keep the longest agreeing prefix, the
-//     target's own token replaces the first wrong guess) and zeroes the
-//     control block for the next launch -- no host memset, so a step can be
-//     replayed from a graph.
+//   * DIRECT: one item per workgroup, dealt by the hardware dispatcher.
+//     A single GEMM, and each job of the step's default M >= 2 schedule
+//     (one launch per job, which measured faster than one persistent launch
+//     there).  With a slice workspace, a narrow matrix's blocks are dealt
+//     as K slices (below) so that every CU has work;
+//   * GRID: resident workgroups walk the lm_head's blocks;
+//   * STATIC: the whole step as one persistent launch: items numbered in
+//     pass order, dealt round-robin to co-resident workgroups.  An item of
+//     stage s (the per-layer order {q,k,v} -> o -> {gate,up} -> down ->
+//     ... -> lm_head) consumes its activations only once stage s-1 is done;
+//     a workgroup issues the item's weight loads FIRST and only then waits.
+//     Completion is signalled once per workgroup and stage, on one of
+//     eight counters per stage; waits are bounded and raise an error flag
+//     instead of hanging.
+//
+// M >= 2, K % 128 == 0 (MfmaLdsItem): the four waves split the block's rows
+// and walk K together in 256-element windows; the activations are staged
+// once per workgroup through an LDS double buffer; weights are dequantised
+// exactly to bf16 (E4M3 x E2M1 has <= 6 significant bits; FP8 E4M3 is exact
+// too) and multiplied on v_mfma_f32_16x16x32_bf16.  A block's sum over K is
+// taken as up to three K slices, each summed from zero, added in slice
+// order -- by the one workgroup that runs them all, or, with the slices
+// dealt as separate items, by the workgroup that completes the block: the
+// same bits either way, no float atomics, bitwise repeatable, and a row's
+// value independent of M.  Other K take the K-split guarded items.  M = 1:
+// GEMV items (a half-wave or a wave per row, v_dot2_f32_bf16 on the
+// unscaled E2M1 values, one FMA per 16-block applies the E4M3 scale).
+//
+// Each weight format is a kernel of its own, and a launch whose every K is
+// a multiple of 128 takes a kernel without the guarded items: one kind's
+// registers do not crowd another's.
+//
+// The lm_head never writes logits: its running best (logit, lowest index)
+// per row -- in a per-wave LDS table with M-tiles -- is published once per
+// workgroup as a 64-bit key with an unsigned atomic max into one of 16
+// slots per row; the last workgroup to leave reads the slots, writes the
+// argmax, runs the accept rule per sequence (TandemLLM README, introduction:
+// keep the longest agreeing prefix, the target's own token replaces the
+// first wrong guess) and zeroes the control block for the next launch -- no
+// host memset, so a step can be replayed from a graph.
 #include <type_traits>
 
 #include "launch.h"

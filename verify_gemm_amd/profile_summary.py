@@ -32,11 +32,37 @@ KERNEL_SOURCES = ["csrc/step_gemv.hip", "csrc/stream.hip", "csrc/nvfp4_device.h"
 PASS_WEIGHT_BYTES = 14115962880
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without comments, blank lines or indentation: what the
+    compiler sees, so that editing a comment does not invalidate counters
+    taken with the same code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":  # a string or character literal, escapes kept
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(ch)
+            i += 1
+    lines = (ln.strip() for ln in "".join(out).splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def sources_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
+        with open(os.path.join(PKG, rel), encoding="utf-8") as f:
+            h.update(rel.encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()
 
 
