@@ -341,7 +341,9 @@ class LmheadJob(ctypes.Structure):
 
 class Pass:
     """A whole step (vg_pass_*): GEMM jobs in dependency order plus an
-    optional lm_head job, run as one persistent launch.  ``gemms`` is a list
+    optional lm_head job.  ``run`` takes the faster schedule for M (one
+    persistent launch at M = 1, one launch per job above),
+    ``run_persistent`` / ``run_unfused`` one of them explicitly.  ``gemms`` is a list
     of (x, wq, ws, gscale, y, stage[, row_scale]) with torch device tensors
     (row_scale: float32 [N] or None, see vg_gemm_job); ``lmhead`` is
     (x, wq, ws, gscale, T, drafts, argmax, accept_len) or None.  ``parents``,

@@ -6,10 +6,11 @@ lm_head (248,320 x 5120) with its fused argmax and greedy accept -- 449
 matrices, 14,115,962,880 weight bytes.  The pages capture each decode step
 as one graph so host launch cost disappears (ling-engine README, "Six
 levers"; the veloGB10 docs list a switch to turn the decode graphs off);
-on MI355X the whole step is ONE persistent launch of the native step
-executor (vg_pass_run), which streams the 449 matrices in the per-layer
-dependency order {q, k, v} -> o -> {gate, up} -> down with device-side stage
-barriers.  The one-launch-per-matrix schedule is kept for comparison.
+on MI355X the native step executor (vg_pass_run) streams the matrices in
+the per-layer dependency order {q, k, v} -> o -> {gate, up} -> down: at
+M = 1 as ONE persistent launch with device-side stage barriers, at M >= 2
+as one launch per job (the faster schedule there); the other schedule of
+each is kept for comparison (run_persistent / run_unfused).
 
 This module only holds device buffers and describes the jobs; all
 sequencing and arithmetic happen in libvgemm.so.
@@ -81,8 +82,9 @@ class PassWeights:
 class PassRun:
     """Activations, outputs and the lm_head buffers for one batch size M on
     top of shared PassWeights, and the step itself as a native vg_pass:
-    ``run()`` is one persistent launch of the whole step, ``run_unfused()``
-    the same work as one launch per matrix.
+    ``run()`` is the step in vg_pass_run's schedule for this M,
+    ``run_persistent()`` one persistent launch of the whole step,
+    ``run_unfused()`` the same work as one launch per job.
 
     ``fused``: {q, k, v} and {gate, up} run as one job each (4 jobs a layer,
     257 in all), reading the members' stacked rows as one matrix; each
