@@ -67,21 +67,39 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_launches(fn, steps, warmup):
+def time_launches(fn, steps, warmup, per_step=None):
     """Average ms of `fn` (work enqueued on the current stream), timed with
-    events recorded on that stream."""
+    events recorded on that stream.  With a list `per_step`, an event
+    between consecutive steps also gives each step's ms (appended to it)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step is not None else 2)]
+    ev[0].record(s)
+    for i in range(steps):
         fn()
-    e1.record(s)
+        if per_step is not None:
+            ev[i + 1].record(s)
+    ev[-1].record(s)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / steps
+
+
+def pass_io_bytes(M: int) -> int:
+    """Algorithmic activation and output bytes of one pass of the timed
+    step (257 jobs): 2*M*K of X in and 4*M*N of Y out per GEMM job, and for
+    the lm_head 2*M*K in and 4*(M + S) out (argmax per row, accept length per
+    sequence; S = M/17 sequences of 17 rows for M >= 17, else M)."""
+    from verify_gemm_amd import synth
+    h, f = synth.HIDDEN, synth.MLP
+    jobs = [(3 * h, h), (h, h), (2 * f, h), (h, f)]  # q|k|v, o, gate|up, down: (N, K)
+    layer = sum(2 * M * k + 4 * M * n for n, k in jobs)
+    seqs = M // 17 if M >= 17 else M
+    return synth.LAYERS * layer + 2 * M * h + 4 * (M + seqs)
 
 
 def bwprobe(device, gib=8, reps=10):
@@ -174,13 +192,19 @@ def main():
         torch.cuda.synchronize()
         if run.check():
             raise RuntimeError(f"M={M}: a stage wait timed out; the step is invalid")
-        ms = time_launches(run.run, args.steps, args.warmup)
+        steps_ms = []
+        ms = time_launches(run.run, args.steps, args.warmup, steps_ms)
         if run.check():
             raise RuntimeError(f"M={M}: a stage wait timed out during timing")
         gbps = wbytes / (ms * 1e-3) / 1e9
+        q = sorted(steps_ms)
+        pct = lambda f: round(q[min(len(q) - 1, int(f * (len(q) - 1) + 0.5))] * 1000, 2)  # noqa: E731
         entry = {"us_per_pass": round(ms * 1000, 2), "weight_gbps": round(gbps, 1),
                  "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-                 "pct_of_probe": round(100 * gbps / probe, 2), "jobs": run.step.info()["jobs"],
+                 "pct_of_probe": round(100 * gbps / probe, 2),
+                 "us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+                 "total_algorithmic_gbps": round((wbytes + pass_io_bytes(M)) / (ms * 1e-3) / 1e9, 1),
+                 "jobs": run.step.info()["jobs"],
                  "schedule": "one persistent launch" if M == 1 else "one launch per job"}
         if M != 1:
             entry["persistent_us_per_pass"] = round(time_launches(run.run_persistent, args.steps, args.warmup) * 1000, 2)

@@ -1,6 +1,6 @@
 """Short text summaries of rocprofv3 output for the profiles/ folder.
 
-Two summaries, each written as Markdown with the exact commands that
+Three summaries, each written as Markdown with the exact commands that
 produced its input:
 
   * ``trace``: the ``--kernel-trace --stats`` kernel statistics of a bench
@@ -14,8 +14,12 @@ produced its input:
     counters were taken with: bench.py reports the traffic only while the
     sources still hash the same.
 
+  * ``busy``: MFMA-busy and VALU-active cycles of the M >= 2 stream
+    kernels from one counter run.
+
     python -m verify_gemm_amd.profile_summary trace STATS_CSV CMD OUT
     python -m verify_gemm_amd.profile_summary pmc FETCH_CSV WRITE_CSV CMD_F CMD_W PROBE_BYTES FILL_BYTES OUT
+    python -m verify_gemm_amd.profile_summary busy COUNTER_CSV CMD OUT
 """
 from __future__ import annotations
 
@@ -173,6 +177,37 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
         f.write("\n".join(lines))
 
 
+# SIMDs per shader engine on MI355X (8 CUs x 4 SIMDs): SQ_BUSY_CYCLES
+# counts an SE's busy cycles, summed over the SEs, while the MFMA-busy and
+# VALU counters sum over every SIMD.
+SIMDS_PER_SE = 32
+BUSY_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def busy(csv_path: str, cmd: str, out: str) -> None:
+    """MFMA and VALU activity per stream kernel from one counter run."""
+    vals = {c: _per_dispatch(csv_path, c)[0] for c in BUSY_COUNTERS}
+    counts = _per_dispatch(csv_path, "SQ_BUSY_CYCLES")[1]
+    lines = ["# MFMA and VALU activity of the M >= 2 stream kernels (rocprofv3 counters)", "",
+             "Command (run from /tmp, `TMPDIR=/tmp`):", "", "```", cmd, "```", "",
+             "| kernel | dispatches | SQ_VALU_MFMA_BUSY_CYCLES | SQ_ACTIVE_INST_VALU | SQ_BUSY_CYCLES | "
+             "MFMA busy | VALU active |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for k in sorted(vals["SQ_BUSY_CYCLES"]):
+        if not k.startswith("stream_kernel"):
+            continue
+        mf, va, sq = (vals[c].get(k, 0.0) for c in BUSY_COUNTERS[:3])
+        den = sq * SIMDS_PER_SE
+        lines.append(f"| {k} | {counts.get(k, 0)} | {mf:.4g} | {va:.4g} | {sq:.4g} | "
+                     f"{100 * mf / den if den else 0:.1f} % | {100 * va / den if den else 0:.1f} % |")
+    lines += ["", "Per dispatch, averaged.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES x "
+              f"{SIMDS_PER_SE}); VALU active the same with SQ_ACTIVE_INST_VALU.  This reads the SQ "
+              "counters as summed over shader engines (busy cycles) and over SIMDs (MFMA, VALU): a share "
+              "of the SIMD cycles while the kernel runs, not an exact utilisation.  MODE 0 kernels are the "
+              "per-job GEMMs of the default schedule, MODE 1 the lm_head, MODE 2 the persistent launch.", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+
+
 def recorded_traffic(path: str):
     """The traffic record of a pmc summary, or None if the summary is
     missing or the kernel sources changed since it was taken."""
@@ -195,6 +230,8 @@ def main(argv):
         trace(argv[2], argv[3], argv[4])
     elif argv[1] == "pmc":
         pmc(argv[2], argv[3], argv[4], argv[5], int(argv[6]), int(argv[7]), argv[8])
+    elif argv[1] == "busy":
+        busy(argv[2], argv[3], argv[4])
     else:
         raise SystemExit(__doc__)
 
