@@ -339,6 +339,13 @@ struct MfmaLdsItem {
   static constexpr int kRows = 16 * NT * kWaves;
   static constexpr int kSlotBytes = 16 * MT * 512;
   static constexpr int kRing = 2;  // slots: the window being read, the next one being written
+  // Five M-tiles hold at most 68 of their 80 rows.  Their two slots are
+  // then M rows apart, not 80: only rows below M are written, and the MFMA
+  // rows past M (whose results are never stored) read what follows -- the
+  // other slot, or a tail that makes the ring VG_MAX_M_DEV + 80 rows.  That
+  // keeps a workgroup's LDS at 75.8 KB, so two fit on a CU.
+  static constexpr bool kCompact = 16 * MT > VG_MAX_M_DEV;
+  static constexpr int kRingBytes = kCompact ? (VG_MAX_M_DEV + 16 * MT) * 512 : kRing * kSlotBytes;
   static constexpr int kXLoads = 2 * MT;  // activation loads per lane per window
   // A lane's 64 weights of a window: NVFP4 32 code bytes + 4 scale bytes;
   // FP8 (E4M3, scales per row in the epilogue) 64 bytes.
@@ -353,6 +360,7 @@ struct MfmaLdsItem {
   unsigned cw, cs, ew;  // this lane's code / scale byte offset within its tile, element offset in a window
   int n0, k, nw, ns;    // first row, K, windows of K, K slices
   int v0, vend, cnt;    // the item's windows [v0, vend), cnt of them
+  int mrows, slot_bytes;  // M; the distance between the two ring slots
   int fs, fold_at;      // whole-block items: the running slice and the window its sum ends after
 
   // Weights are loaded with the default cache policy: the scale bytes of
@@ -428,7 +436,8 @@ struct MfmaLdsItem {
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
       const int m = xrow(i);
-      *reinterpret_cast<u32x4*>(slot + 512 * m + 16 * (piece ^ (unsigned)(m & 15))) = xq[p][i];
+      if (!kCompact || m < mrows)
+        *reinterpret_cast<u32x4*>(slot + 512 * m + 16 * (piece ^ (unsigned)(m & 15))) = xq[p][i];
     }
   }
 
@@ -474,9 +483,11 @@ struct MfmaLdsItem {
   }
 
   // After the stage wait: the activations of the first P windows, then
-  // every window in order.  `lds` holds kRing slots of kSlotBytes.
+  // every window in order.  `lds` holds the ring (kRingBytes).
   __device__ __forceinline__ void compute(const StreamJob& j, int M, unsigned char* lds) {
     rx = rsrc_uniform(j.x, (unsigned)M * (unsigned)j.k * 2u);
+    mrows = M;
+    slot_bytes = kCompact ? 512 * M : kSlotBytes;
 #pragma unroll
     for (int p = 0; p < P; ++p) load_x(p, v0 + p);
 #pragma unroll
@@ -531,10 +542,10 @@ struct MfmaLdsItem {
   __device__ __forceinline__ void step(int p, int i, unsigned char* lds) {
     __syncthreads();  // window i is in LDS; every wave is done with window i-1
     if (i < cnt) {    // wave-uniform; nothing in here loads from memory
-      window(p, lds + (i & 1) * kSlotBytes);
+      window(p, lds + (i & 1) * slot_bytes);
       if (v0 + i + 1 == fold_at) fold();
     }
-    store_x(p + 1 < P ? p + 1 : 0, lds + ((i + 1) & 1) * kSlotBytes);
+    store_x(p + 1 < P ? p + 1 : 0, lds + ((i + 1) & 1) * slot_bytes);
     load_x(p, v0 + i + P);
     load_w(p, v0 + i + P);
   }
@@ -1127,13 +1138,16 @@ __device__ void finish_lmhead(StreamCtl* ctl, const StreamArgs& a, int* lds_am, 
 template <int MT, int MODE, int FMT, int ANYK>
 // Two M-tiles: registers capped for two waves per SIMD, so the step can
 // keep two workgroups per CU (measured: the M = 17 step 4 % faster; one
-// M-tile and three or more gain nothing or lose).
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(MT == 2 ? 2 : 1))) void stream_kernel(
+// M-tile and three or four gain nothing or lose).  Five M-tiles, one
+// launch per GEMM: the compact ring lets two workgroups share a CU, and
+// the cap makes their registers fit (M = 68 per-job step 6 % faster).
+__global__ __launch_bounds__(kWG)
+__attribute__((amdgpu_waves_per_eu(MT == 2 || (MT == 5 && MODE == MODE_DIRECT) ? 2 : 1))) void stream_kernel(
     StreamArgs a) {
   constexpr int NT = MT == 0 ? 1 : Cfg<MT>::NT;
   constexpr int kRed = MT == 0 ? 1 : (kWaves - 1) * MT * NT * 4 * kWave;
   __shared__ float red[kRed];
-  constexpr int kXRing = MT == 0 ? 16 : Cfg<(MT > 0 ? MT : 1)>::Lds::kRing * Cfg<(MT > 0 ? MT : 1)>::Lds::kSlotBytes;
+  constexpr int kXRing = MT == 0 ? 16 : Cfg<(MT > 0 ? MT : 1)>::Lds::kRingBytes;
   __shared__ __attribute__((aligned(16))) unsigned char xring[kXRing];
   __shared__ int lds_flag;
   __shared__ int lds_am[VG_MAX_M_DEV];
