@@ -25,7 +25,8 @@
 //
 // M >= 2, K % 128 == 0 (MfmaLdsItem): the four waves split the block's rows
 // and walk K together in 256-element windows; the activations are staged
-// once per workgroup through an LDS double buffer; weights are dequantised
+// once per workgroup through an LDS double buffer (with five M-tiles its
+// slots sit M rows apart, so two workgroups fit on a CU); weights are dequantised
 // exactly to bf16 (E4M3 x E2M1 has <= 6 significant bits; FP8 E4M3 is exact
 // too) and multiplied on v_mfma_f32_16x16x32_bf16.  A block's sum over K is
 // taken as up to three K slices, each summed from zero, added in slice
