@@ -171,3 +171,29 @@ def test_workspace_reused_across_shapes():
         y_ref, bound = oracle.nvfp4_gemm_ref(x, wq, ws, 1.0)
         ok, worst, at = within_bound(y, y_ref, bound)
         assert ok, f"M={m} N={n} K={k}: worst err/bound {worst:.3g} at {at}"
+
+
+def _random_shape(case):
+    """Seeded shape of sweep case `case`: M over 1..68 (every fourth case in
+    65..68, the five-tile range), N ragged, K a multiple of 128 (the
+    shared-activation item) or only of 16 (the guarded item)."""
+    rng = np.random.default_rng(9900 + case)
+    m = int(rng.integers(65, 69)) if case % 4 == 0 else int(rng.integers(1, 69))
+    n = int(rng.integers(1, 900))
+    k = 128 * int(rng.integers(1, 41)) if case % 2 == 0 else 16 * int(rng.integers(1, 321))
+    return rng, m, n, k
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes(case):
+    """A seeded sweep of shapes off the tuned grid.  Each case: the oracle's
+    bound, and, where a workspace applies (K slices dealt to separate
+    workgroups), the same bits with and without it."""
+    rng, m, n, k = _random_shape(case)
+    wq, ws = synth.gen_weights(rng, n, k)
+    x = synth.gen_x(rng, m, k)
+    g = float(rng.uniform(0.25, 2.0))
+    y = check(x, wq, ws, g, f"sweep case {case}")
+    if binding.gemm_workspace_bytes(m, n, k) > 0:
+        y_ws = run_gemm(x, wq, ws, g, workspace=True)
+        assert np.array_equal(y_ws.view(np.uint32), y.view(np.uint32)), "sliced launch changed the bits"
