@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1024, 5120), (1, 300, 1040), (1, 77, 48), (4, 100, 4096),
-                                   (17, 512, 5120), (17, 96, 17408), (68, 256, 1024), (68, 33, 80)])
+                                   (17, 512, 5120), (17, 96, 17408), (68, 256, 1024), (68, 33, 80),
+                                   (65, 700, 2048), (67, 129, 4096)])
 @pytest.mark.parametrize("with_rs", [True, False])
 def test_fp8_gemm_matches_oracle(m, n, k, with_rs):
     print(f"[case] fp8_gemm M={m} N={n} K={k} row_scale={with_rs}", flush=True)
@@ -31,7 +32,7 @@ def test_fp8_gemm_matches_oracle(m, n, k, with_rs):
     assert guards_intact(buf, pad), "a write landed outside Y"
 
 
-@pytest.mark.parametrize("M,T", [(1, 1), (17, 17), (68, 17)])
+@pytest.mark.parametrize("M,T", [(1, 1), (17, 17), (68, 17), (66, 33)])
 def test_fp8_lmhead_verify(M, T):
     print(f"[case] fp8 lm_head M={M} T={T}", flush=True)
     rng = np.random.default_rng(46000 + M)

@@ -65,7 +65,8 @@ def check(x, wq, ws, g, T, rng, label):
     return int(nd.sum())
 
 
-@pytest.mark.parametrize("m,T", [(1, 1), (2, 2), (4, 1), (17, 17), (34, 17), (68, 17), (68, 68), (5, 5)])
+@pytest.mark.parametrize("m,T", [(1, 1), (2, 2), (4, 1), (17, 17), (34, 17), (68, 17), (68, 68), (5, 5),
+                                 (65, 13), (66, 33), (67, 67)])
 @pytest.mark.parametrize("k,v", [(5120, 1000), (1024, 4099), (48, 77), (272, 1)])
 def test_small_lmhead(m, T, k, v):
     rng = np.random.default_rng(20000 + m * 101 + T * 7 + k + v)
