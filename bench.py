@@ -164,7 +164,7 @@ def recorded_traffic(kernel: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: there is no multi-GPU path in this build "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(how the step would shard is described, not implemented); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
