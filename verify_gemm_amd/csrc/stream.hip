@@ -28,7 +28,9 @@
 // once per workgroup through an LDS double buffer (with five M-tiles its
 // slots sit M rows apart, so two workgroups fit on a CU); weights are dequantised
 // exactly to bf16 (E4M3 x E2M1 has <= 6 significant bits; FP8 E4M3 is exact
-// too) and multiplied on v_mfma_f32_16x16x32_bf16.  A block's sum over K is
+// too) and multiplied on v_mfma_f32_16x16x32_bf16.  With a four-window ring
+// a row's scales are fetched once per four windows and passed between the
+// row's lanes through LDS.  A block's sum over K is
 // taken as up to three K slices, each summed from zero, added in slice
 // order -- by the one workgroup that runs them all, or, with the slices
 // dealt as separate items, by the workgroup that completes the block: the
@@ -347,13 +349,22 @@ struct MfmaLdsItem {
   // keeps a workgroup's LDS at 75.8 KB, so two fit on a CU.
   static constexpr bool kCompact = 16 * MT > VG_MAX_M_DEV;
   static constexpr int kRingBytes = kCompact ? (VG_MAX_M_DEV + 16 * MT) * 512 : kRing * kSlotBytes;
+  // NVFP4 with a four-window ring: a row's scales are loaded once per group
+  // of four windows, one 16-byte piece (one window, all four quarters) per
+  // lane, and passed between the row's four lanes through a per-wave table
+  // (16 rows of 17 dwords: the odd stride spreads the reads over the banks).
+  // Four times fewer scale requests; every window sees the same bytes.
+  static constexpr bool kGroupScales = FMT == 0 && P == 4;
+  static constexpr int kScaleTable = 16 * 17;  // dwords per wave and 16-row tile
+  static constexpr int kLdsBytes = kRingBytes + (kGroupScales ? kWaves * NT * kScaleTable * 4 : 0);
   static constexpr int kXLoads = 2 * MT;  // activation loads per lane per window
   // A lane's 64 weights of a window: NVFP4 32 code bytes + 4 scale bytes;
   // FP8 (E4M3, scales per row in the epilogue) 64 bytes.
   static constexpr int kQ = FMT == 0 ? 2 : 4;        // 16-byte weight loads per lane per window
   static constexpr unsigned kLaneBytes = 16u * kQ;   // a lane's weight bytes per window
   u32x4 q[P][NT][kQ];
-  unsigned sc[P][NT];
+  unsigned sc[P][NT];     // per window: this lane's four scale bytes
+  u32x4 sg[NT];          // grouped scales in flight: one window's 16 bytes of this lane's row
   u32x4 xq[P][kXLoads];  // this wave's rows of the activation window, per ring position
   f32x4 acc[MT][NT];     // the running slice's sum; after compute(), the result (see fold)
   f32x4 tot[MT][NT];     // sum of the finished slices (whole-block items)
@@ -375,8 +386,16 @@ struct MfmaLdsItem {
 #pragma unroll
       for (int t = 0; t < kQ; ++t)
         q[p][nt][t] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? o + 16u * t : kOOB, 0, 0);
-      if constexpr (FMT == 0)
+      if constexpr (kGroupScales) {
+        if (p == 0) {  // the group starting at window v: window v + gq of this lane's row
+          const unsigned gq = (threadIdx.x & 63) >> 4;
+          const bool gin = v + (int)gq < vend;
+          sg[nt] = __builtin_amdgcn_raw_buffer_load_b128(rs[nt], gin ? cs - 4u * gq + 16u * ((unsigned)v + gq) : kOOB,
+                                                         0, 0);
+        }
+      } else if constexpr (FMT == 0) {
         sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b32(rs[nt], in ? cs + 16u * (unsigned)v : kOOB, 0, 0);
+      }
     }
   }
 
@@ -446,6 +465,30 @@ struct MfmaLdsItem {
   // step st multiplies (two register sets): with the reads of a step issued
   // only after the previous step's MFMAs, every step waited one LDS round
   // trip, and with one wave per SIMD nothing else hid it.
+  // Group start (window v, ring position 0): lane (c, gq) holds window
+  // v + gq's 16 scale bytes of row c; after the exchange, sc[t] holds
+  // window v + t's bytes 4gq .. 4gq+3 -- zero where those elements lie past
+  // K (a half window's other half may read the next row's scales).
+  __device__ __forceinline__ void spread_scales(int v, unsigned* table) {
+    const unsigned lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      unsigned* t0 = table + nt * kScaleTable + 17 * c;
+      t0[4 * gq + 0] = sg[nt].x;
+      t0[4 * gq + 1] = sg[nt].y;
+      t0[4 * gq + 2] = sg[nt].z;
+      t0[4 * gq + 3] = sg[nt].w;
+      // other lanes' writes are read next: the wave's LDS operations run in
+      // order; the fence keeps the compiler from moving the reads up
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+#pragma unroll
+      for (int t = 0; t < P; ++t) {
+        const unsigned word = t0[4 * t + gq];
+        sc[t][nt] = 256u * (unsigned)(v + t) + ew < (unsigned)k ? word : 0u;
+      }
+    }
+  }
+
   __device__ __forceinline__ void window(int p, const unsigned char* slot) {
     const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
     f32x2 s[NT][2];
@@ -542,6 +585,9 @@ struct MfmaLdsItem {
   // v0 + i + P into position p.
   __device__ __forceinline__ void step(int p, int i, unsigned char* lds) {
     __syncthreads();  // window i is in LDS; every wave is done with window i-1
+    if constexpr (kGroupScales)
+      if (p == 0) spread_scales(v0 + i, reinterpret_cast<unsigned*>(lds + kRingBytes) +
+                                            (threadIdx.x >> 6) * NT * kScaleTable);
     if (i < cnt) {    // wave-uniform; nothing in here loads from memory
       window(p, lds + (i & 1) * slot_bytes);
       if (v0 + i + 1 == fold_at) fold();
@@ -1141,14 +1187,19 @@ template <int MT, int MODE, int FMT, int ANYK>
 // keep two workgroups per CU (measured: the M = 17 step 4 % faster; one
 // M-tile and three or four gain nothing or lose).  Five M-tiles, one
 // launch per GEMM: the compact ring lets two workgroups share a CU, and
-// the cap makes their registers fit (M = 68 per-job step 6 % faster).
+// the cap makes their registers fit (M = 68 per-job step 6 % faster).  One
+// M-tile, NVFP4, one launch per GEMM: capped at four waves per SIMD, which
+// the grouped scales had just pushed it past (M = 4 per-job step 1 % faster;
+// the FP8 kernel would spill).
 __global__ __launch_bounds__(kWG)
-__attribute__((amdgpu_waves_per_eu(MT == 2 || (MT == 5 && MODE == MODE_DIRECT) ? 2 : 1))) void stream_kernel(
+__attribute__((amdgpu_waves_per_eu(MT == 1 && MODE == MODE_DIRECT && FMT == 0 ? 4
+                                   : MT == 2 || (MT == 5 && MODE == MODE_DIRECT) ? 2
+                                                                                  : 1))) void stream_kernel(
     StreamArgs a) {
   constexpr int NT = MT == 0 ? 1 : Cfg<MT>::NT;
   constexpr int kRed = MT == 0 ? 1 : (kWaves - 1) * MT * NT * 4 * kWave;
   __shared__ float red[kRed];
-  constexpr int kXRing = MT == 0 ? 16 : Cfg<(MT > 0 ? MT : 1)>::Lds::kRingBytes;
+  constexpr int kXRing = MT == 0 ? 16 : Cfg<(MT > 0 ? MT : 1)>::Lds::kLdsBytes;
   __shared__ __attribute__((aligned(16))) unsigned char xring[kXRing];
   __shared__ int lds_flag;
   __shared__ int lds_am[VG_MAX_M_DEV];
