@@ -28,9 +28,9 @@
 // once per workgroup through an LDS double buffer (with five M-tiles its
 // slots sit M rows apart, so two workgroups fit on a CU); weights are dequantised
 // exactly to bf16 (E4M3 x E2M1 has <= 6 significant bits; FP8 E4M3 is exact
-// too) and multiplied on v_mfma_f32_16x16x32_bf16.  With a four-window ring
-// a row's scales are fetched once per four windows and passed between the
-// row's lanes through LDS.  A block's sum over K is
+// too) and multiplied on v_mfma_f32_16x16x32_bf16.  A row's NVFP4 scales
+// are fetched once per group of ring windows and passed between the row's
+// lanes through LDS.  A block's sum over K is
 // taken as up to three K slices, each summed from zero, added in slice
 // order -- by the one workgroup that runs them all, or, with the slices
 // dealt as separate items, by the workgroup that completes the block: the
@@ -349,12 +349,14 @@ struct MfmaLdsItem {
   // keeps a workgroup's LDS at 75.8 KB, so two fit on a CU.
   static constexpr bool kCompact = 16 * MT > VG_MAX_M_DEV;
   static constexpr int kRingBytes = kCompact ? (VG_MAX_M_DEV + 16 * MT) * 512 : kRing * kSlotBytes;
-  // NVFP4 with a four-window ring: a row's scales are loaded once per group
-  // of four windows, one 16-byte piece (one window, all four quarters) per
-  // lane, and passed between the row's four lanes through a per-wave table
-  // (16 rows of 17 dwords: the odd stride spreads the reads over the banks).
-  // Four times fewer scale requests; every window sees the same bytes.
-  static constexpr bool kGroupScales = FMT == 0 && P == 4;
+  // NVFP4: a row's scales are loaded once per group of P windows (16P
+  // contiguous bytes), 4P bytes per lane -- with P = 4 one window's four
+  // quarters, with P = 2 half a window -- and passed between the row's four
+  // lanes through a per-wave table (16 rows of 17 dwords: the odd stride
+  // spreads the reads over the banks).  P times fewer scale requests; every
+  // window sees the same bytes.
+  static constexpr bool kGroupScales = FMT == 0 && (P == 4 || P == 2);
+  using ScaleLoad = std::conditional_t<P == 4, u32x4, u32x2>;
   static constexpr int kScaleTable = 16 * 17;  // dwords per wave and 16-row tile
   static constexpr int kLdsBytes = kRingBytes + (kGroupScales ? kWaves * NT * kScaleTable * 4 : 0);
   static constexpr int kXLoads = 2 * MT;  // activation loads per lane per window
@@ -364,7 +366,7 @@ struct MfmaLdsItem {
   static constexpr unsigned kLaneBytes = 16u * kQ;   // a lane's weight bytes per window
   u32x4 q[P][NT][kQ];
   unsigned sc[P][NT];     // per window: this lane's four scale bytes
-  u32x4 sg[NT];          // grouped scales in flight: one window's 16 bytes of this lane's row
+  ScaleLoad sg[NT];      // grouped scales in flight: 4P bytes of this lane's row
   u32x4 xq[P][kXLoads];  // this wave's rows of the activation window, per ring position
   f32x4 acc[MT][NT];     // the running slice's sum; after compute(), the result (see fold)
   f32x4 tot[MT][NT];     // sum of the finished slices (whole-block items)
@@ -387,11 +389,14 @@ struct MfmaLdsItem {
       for (int t = 0; t < kQ; ++t)
         q[p][nt][t] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], in ? o + 16u * t : kOOB, 0, 0);
       if constexpr (kGroupScales) {
-        if (p == 0) {  // the group starting at window v: window v + gq of this lane's row
+        if (p == 0) {  // the group starting at window v: bytes 4P*gq .. of its 16P
           const unsigned gq = (threadIdx.x & 63) >> 4;
-          const bool gin = v + (int)gq < vend;
-          sg[nt] = __builtin_amdgcn_raw_buffer_load_b128(rs[nt], gin ? cs - 4u * gq + 16u * ((unsigned)v + gq) : kOOB,
-                                                         0, 0);
+          const bool gin = v + (int)(P * gq / 4) < vend;
+          const unsigned off = gin ? cs - 4u * gq + 16u * (unsigned)v + 4u * P * gq : kOOB;
+          if constexpr (P == 4)
+            sg[nt] = __builtin_amdgcn_raw_buffer_load_b128(rs[nt], off, 0, 0);
+          else
+            sg[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs[nt], off, 0, 0);
         }
       } else if constexpr (FMT == 0) {
         sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b32(rs[nt], in ? cs + 16u * (unsigned)v : kOOB, 0, 0);
@@ -465,19 +470,18 @@ struct MfmaLdsItem {
   // step st multiplies (two register sets): with the reads of a step issued
   // only after the previous step's MFMAs, every step waited one LDS round
   // trip, and with one wave per SIMD nothing else hid it.
-  // Group start (window v, ring position 0): lane (c, gq) holds window
-  // v + gq's 16 scale bytes of row c; after the exchange, sc[t] holds
-  // window v + t's bytes 4gq .. 4gq+3 -- zero where those elements lie past
-  // K (a half window's other half may read the next row's scales).
+  // Group start (window v, ring position 0): lane (c, gq) holds bytes
+  // 4P*gq .. 4P*gq+4P-1 of row c's 16P scale bytes of windows v .. v+P-1;
+  // after the exchange, sc[t] holds window v + t's bytes 4gq .. 4gq+3 --
+  // zero where those elements lie past K (a half window's other half may
+  // read the next row's scales).
   __device__ __forceinline__ void spread_scales(int v, unsigned* table) {
     const unsigned lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       unsigned* t0 = table + nt * kScaleTable + 17 * c;
-      t0[4 * gq + 0] = sg[nt].x;
-      t0[4 * gq + 1] = sg[nt].y;
-      t0[4 * gq + 2] = sg[nt].z;
-      t0[4 * gq + 3] = sg[nt].w;
+#pragma unroll
+      for (int d = 0; d < P; ++d) t0[P * gq + d] = sg[nt][d];
       // other lanes' writes are read next: the wave's LDS operations run in
       // order; the fence keeps the compiler from moving the reads up
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
