@@ -346,7 +346,8 @@ struct MfmaLdsItem {
   // then M rows apart, not 80: only rows below M are written, and the MFMA
   // rows past M (whose results are never stored) read what follows -- the
   // other slot, or a tail that makes the ring VG_MAX_M_DEV + 80 rows.  That
-  // keeps a workgroup's LDS at 75.8 KB, so two fit on a CU.
+  // keeps the ring at 75.8 KB (80.1 KB with the scale table below), so two
+  // workgroups fit on a CU.
   static constexpr bool kCompact = 16 * MT > VG_MAX_M_DEV;
   static constexpr int kRingBytes = kCompact ? (VG_MAX_M_DEV + 16 * MT) * 512 : kRing * kSlotBytes;
   // NVFP4: a row's scales are loaded once per group of P windows (16P
