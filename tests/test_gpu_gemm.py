@@ -197,3 +197,23 @@ def test_random_shapes(case):
     if binding.gemm_workspace_bytes(m, n, k) > 0:
         y_ws = run_gemm(x, wq, ws, g, workspace=True)
         assert np.array_equal(y_ws.view(np.uint32), y.view(np.uint32)), "sliced launch changed the bits"
+
+
+@pytest.mark.parametrize("m", [1, 4, 17, 33, 68])
+def test_half_window_scales_stay_in_their_row(m):
+    """K = 1152 ends in half a 256-element window, whose scale fetch also
+    covers the first bytes of the next row's scales.  Row 1's first scale
+    byte is the E4M3 NaN pattern: row 1's outputs are NaN (as the oracle
+    says), and rows 0 and 2 must be untouched by it."""
+    rng = np.random.default_rng(9950 + m)
+    n, k = 3, 1152
+    wq, ws = synth.gen_weights(rng, n, k)
+    ws[1, 0] = 0x7F
+    x = synth.gen_x(rng, m, k)
+    print(f"[case] half-window scales M={m} N={n} K={k}", flush=True)
+    y = run_gemm(x, wq, ws, 1.0)
+    y_ref, bound = oracle.nvfp4_gemm_ref(x, wq, ws, 1.0)
+    assert np.isnan(y_ref[:, 1]).all() and np.isnan(y[:, 1]).all()
+    keep = [0, 2]
+    ok, worst, at = within_bound(y[:, keep], y_ref[:, keep], bound[:, keep])
+    assert ok, f"worst err/bound {worst:.3g} at {at}"
