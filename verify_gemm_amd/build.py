@@ -1,26 +1,32 @@
 """Build libvgemm.so in-tree with hipcc for gfx950.
 
 ``python -m verify_gemm_amd.build`` (or ``__graft_entry__.build()``)
-compiles every HIP source under ``csrc/`` into ``verify_gemm_amd/libvgemm.so``.
+compiles every HIP source under ``csrc/`` into ``verify_gemm_amd/libvgemm.so``:
+each source to an object file (in parallel: the stream kernel's variants
+sit in one translation unit per M-tile class and weight format), then one
+link.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvgemm.so")
-SOURCES = ["api.cpp", "stream.hip", "step_gemv.hip", "bwprobe.hip"]
+SOURCES = (["api.cpp", "stream.hip", "step_gemv.hip", "bwprobe.hip"]
+           + [f"stream_mt{mt}_f{fmt}.hip" for mt in range(6) for fmt in range(2)])
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code: hipcc may form
 # them from ordinary float code, and they are not needed on this path.
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", "-Wno-inline-asm", "-I", os.path.join(ROOT, "include"),
 ]
@@ -33,16 +39,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libvgemm.so)")
 
 
+def _jobs() -> int:
+    env = os.environ.get("MAX_JOBS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def build(verbose: bool = False) -> str:
     """Compile libvgemm.so (always rebuilds).  Returns its path."""
-    out_tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="vgemm_build_") as tmp:
+        def compile_one(src):
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            return src, obj, res
+
+        # the slowest translation units first
+        order = sorted(SOURCES, key=lambda f: (not f.startswith("stream_mt"), f))
+        with concurrent.futures.ThreadPoolExecutor(_jobs()) as ex:
+            results = list(ex.map(compile_one, order))
+        for src, _, res in results:
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError(f"hipcc failed on {src} with exit code {res.returncode}")
+        out_tmp = LIB + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-fPIC", "-shared", *[obj for _, obj, _ in results], "-o", out_tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(out_tmp, LIB)
     return LIB
 

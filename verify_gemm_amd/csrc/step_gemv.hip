@@ -112,7 +112,16 @@ constexpr int kScaleDma = (kMaxChunkScale + 1023) / 1024;
 constexpr int kScaleBufs = 3;  // chunks k, k+1 (ready) and k+2 (in flight)
 constexpr unsigned kOOB = 0x80000000u;  // buffer offset past every range used here
 constexpr int kNT = 2;                  // buffer-load cache policy: nontemporal
-constexpr long kSpinLimit = 1L << 22;   // polls (with sleeps) before giving up
+// Bounded waits measure wall-clock time on the GPU's constant 100 MHz
+// counter (s_memrealtime).  A stage wait gives up after half a second.  The
+// waits between the roles of one workgroup only ever wait for work that is
+// at most one stage wait (plus a chunk's compute) away, so their limit is
+// eight times longer: they never expire while the I/O wave still waits for
+// a stage, and a stage time-out alone raises the error flag.
+constexpr unsigned long long kTicksPerSecond = 100000000ull;
+constexpr unsigned long long kStageWaitTicks = kTicksPerSecond / 2;
+constexpr unsigned long long kLocalWaitTicks = 4 * kTicksPerSecond;
+__device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
 // s_waitcnt immediate for vmcnt(0) (gfx9 encoding: vmcnt[3:0]+[15:14],
 // expcnt[6:4], lgkmcnt[11:8]; the other two fields at "no wait").
@@ -485,11 +494,19 @@ __device__ __forceinline__ void compute_loop(const StreamArgs& a, Shared& sh, in
 
 // ---- I/O wave ----------------------------------------------------------
 
+// A bounded wait gave up: raise the launch's error flag.  A single GEMM
+// launch has no control block (it waits on no stage); then the wait just
+// ends and the launch runs on.
+__device__ __forceinline__ void raise_error(const StreamArgs& a, int lane) {
+  if (lane == 0 && a.ctl) st_agent(&a.ctl->error, 1u);
+}
+
 // Polls until `target` workgroups have signalled stage `s` (whole wave,
 // uniform result), then acquires at agent scope.
 __device__ bool wait_stage(const StreamArgs& a, int s, unsigned target) {
   const int lane = threadIdx.x & 63;
-  for (long it = 0; it < kSpinLimit; ++it) {
+  const unsigned long long t0 = now_ticks();
+  for (;;) {
     unsigned v = lane < kDoneSlots ? ld_agent(&a.stage_done[s][lane].v) : 0u;
 #pragma unroll
     for (int off = kDoneSlots / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
@@ -497,24 +514,27 @@ __device__ bool wait_stage(const StreamArgs& a, int s, unsigned target) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       return true;
     }
+    if (now_ticks() - t0 > kStageWaitTicks) break;
     __builtin_amdgcn_s_sleep(2);
   }
-  if (lane == 0) st_agent(&a.ctl->error, 1u);
+  raise_error(a, lane);
   return false;
 }
 
 // Waits until every compute wave has finished the chunk of `parity`.  The
 // compute waves need nothing more from this wave to finish a released
-// chunk, so the wait ends; it is bounded all the same.
+// chunk, so the wait ends; it is bounded all the same (kLocalWaitTicks).
 __device__ bool wait_done(const StreamArgs& a, Shared& sh, int parity) {
-  for (long it = 0; it < kSpinLimit; ++it) {
+  const unsigned long long t0 = now_ticks();
+  for (;;) {
     if (__hip_atomic_load(&sh.done[parity], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= (unsigned)kCW) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       return true;
     }
+    if (now_ticks() - t0 > kLocalWaitTicks) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  if ((threadIdx.x & 63) == 0) st_agent(&a.ctl->error, 1u);
+  raise_error(a, threadIdx.x & 63);
   return false;
 }
 
@@ -611,14 +631,16 @@ __device__ __forceinline__ void release(Shared& sh, unsigned n) {
 // Waits until the results of chunk ordinals below n are stored.  The store
 // wave needs nothing from this wave for chunks already released.
 __device__ bool wait_flushed(const StreamArgs& a, const Shared& sh, unsigned n) {
-  for (long it = 0; it < kSpinLimit; ++it) {
+  const unsigned long long t0 = now_ticks();
+  for (;;) {
     if (lds_load(&sh.flushed) >= n) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       return true;
     }
+    if (now_ticks() - t0 > kLocalWaitTicks) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  if ((threadIdx.x & 63) == 0) st_agent(&a.ctl->error, 1u);
+  raise_error(a, threadIdx.x & 63);
   return false;
 }
 

@@ -32,7 +32,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # Sources whose change invalidates recorded counter values.
-KERNEL_SOURCES = ["csrc/step_gemv.hip", "csrc/stream.hip", "csrc/nvfp4_device.h", "csrc/launch.h"]
+KERNEL_SOURCES = ["csrc/step_gemv.hip", "csrc/stream_kernel.h", "csrc/nvfp4_device.h", "csrc/launch.h"]
 PASS_WEIGHT_BYTES = 14115962880
 
 
