@@ -207,19 +207,24 @@ def test_pass_batch_invariant_rows_and_tree():
     p17.close()
 
 
-@pytest.mark.parametrize("M", [1, 4, 17])
+@pytest.mark.parametrize("M", [1, 4, 17, 33, 52, 68])
 def test_row_scales_stack_matrices_bitwise(M):
     """Two matrices stacked by rows as one job with per-row scales (each
     member's own tensor scale) give the same bits as two jobs, in the
-    one-launch and one-launch-per-job schedules; K = 5120 (step kernel at
-    M = 1) and K = 48 (the stream kernel's generic path).  304 rows keep the
-    second member's code and scale rows 16-byte aligned at both K."""
+    one-launch and one-launch-per-job schedules, and lie within the
+    oracle's bound with each member's own g.  K = 5120 and 17408 (the step
+    kernel at M = 1; the LDS-shared MFMA item with one to five M-tiles
+    above, the five-tile compact ring at M = 68, K slices dealt as separate
+    items in the step) and K = 48 (the stream kernel's guarded path).  304
+    rows keep the second member's code and scale rows 16-byte aligned at
+    every K."""
     print(f"[case] row scales M={M}", flush=True)
     rng = np.random.default_rng(44000 + M)
-    for k in (5120, 48):
+    for k in (5120, 17408, 48):
         parts = [synth.gen_weights(rng, n, k) for n in (304, 208)]
         gs = [synth.gen_gscale(rng), synth.gen_gscale(rng)]
-        x = dev_bf16(synth.gen_x(rng, M, k))
+        xh = synth.gen_x(rng, M, k)
+        x = dev_bf16(xh)
         wq = dev_u8(np.concatenate([p[0] for p in parts]))
         ws = dev_u8(np.concatenate([p[1] for p in parts]))
         rs = torch.cat([torch.full((304,), gs[0]), torch.full((208,), gs[1])]).float().cuda()
@@ -233,6 +238,14 @@ def test_row_scales_stack_matrices_bitwise(M):
             getattr(sep, run)()
             getattr(fus, run)()
             torch.cuda.synchronize()
+            assert sep.check() == 0 and fus.check() == 0, f"K={k} {run}: a stage wait timed out"
             assert same_bits(yf, torch.cat([ya, yb], 1)), f"K={k} {run}"
+        yh = yf.cpu().numpy()
+        c0 = 0
+        for (pq, ps), g in zip(parts, gs):
+            y_ref, bound = oracle.nvfp4_gemm_ref(xh, pq, ps, g)
+            ok, worst, at = within_bound(yh[:, c0:c0 + pq.shape[0]], y_ref, bound)
+            assert ok, f"K={k} member at column {c0}: worst err/bound {worst:.3g} at {at}"
+            c0 += pq.shape[0]
         sep.close()
         fus.close()
