@@ -1,36 +1,38 @@
-"""Benchmark: the full NVFP4 weight pass of a decode / verify step on one MI355X.
+"""Benchmark: the NVFP4 weight pass of a decode / verify step on one MI355X.
 
 One step = one pass over the whole hot path: 64 layers x {q, k, v, o, gate,
 up, down} NVFP4 GEMMs + the lm_head with fused argmax and greedy accept
 (449 matrices, 14,115,962,880 weight bytes), run by the native step
 executor (vg_pass_run) in its faster schedule: ONE persistent kernel launch
-at M = 1, one launch per job at M >= 2 (there the hardware dispatcher
-balances each matrix's blocks; the persistent launch is timed beside it as
-``persistent_us_per_pass``).  Each layer's q, k, v (and
-gate, up) are stored back to back and read as one stacked matrix -- 257 jobs
--- with each member's own tensor scale kept as per-row scales, so every
-output has the same bits as with 449 separate jobs (the fused projections
-of dgx-spark-qwen38 README, opening section).  Reported at M = 1 (plain
-decode), 4, 17 (16 drafts + 1) and 68 (4 sequences x 17): microseconds per
-pass and effective weight GB/s against the 8 TB/s HBM peak.  ``value`` is
-the M = 1 figure; every batch size is in ``per_m``.
+at M = 1, one launch per job at M >= 2.  Reported at M = 1 (plain decode),
+4, 17 (16 drafts + 1) and 68 (4 sequences x 17): microseconds per pass and
+effective weight GB/s against the 8 TB/s HBM peak.  ``value`` is the M = 1
+figure of the 449-job step; every batch size is in ``per_m``.
 
-Also measured in the same run:
-  * the read ceiling of a pure streaming-read kernel (vg_bwprobe);
-  * the same step as one launch per job, captured in a HIP graph
-    (``unfused_graph_us_per_pass``), and as 449 separate jobs, one launch
-    and one launch per job (``separate_jobs``): the schedules the single
-    launch replaces;
-  * ``roofline``: the dominant kernel is the step kernel itself (the whole
-    pass is one launch): 14,115,962,880 weight bytes per launch over its
-    event-timed average duration at the first M;
-  * ``roofline.traffic``: HBM bytes per launch of that kernel from the
-    committed rocprofv3 counter summary (profiles/), null once the kernel
-    sources differ from the ones the counters were taken with;
-  * the CPU oracle on a bounded sample (whole layers at M = 1, about 12 s
-    of oracle time) on this host's cores -> ``cpu_baseline``.
+Also measured in the same run (all inputs seeded, synthetic, resident in
+HBM before any timed region):
+  * ``per_m[M].fused``: the same step with each layer's {q, k, v} and
+    {gate, up} read as one stacked matrix (257 jobs, each member's tensor
+    scale kept as per-row scales, outputs bit-identical to 449 jobs) -- the
+    fused projections of dgx-spark-qwen38 README, opening section;
+  * ``per_m[M].roofline``: the pass against the HBM roofline (and at
+    M = 68 the bf16 MFMA roofline too);
+  * ``configs``: the single matrices of the decode GEMV (M = 1: 17408 x 5120
+    and 5120 x 5120) and the verify GEMM (M = 17: 5120 x 17408 and
+    17408 x 5120), each timed over >= 1 GiB of distinct rotating weight
+    copies so every launch reads HBM, not the 256 MB last-level cache; the
+    lm_head verify (M = 17, K = 5120) at V = 248,320 and its 65,536-row
+    slice over 1000 seeded steps, checked against the stored oracle results
+    (near ties counted); FP8 17408 x 5120 GEMMs at M = 1, 17, 68;
+  * ``bwprobe_read_gbps``: the pure streaming-read ceiling (vg_bwprobe);
+  * ``roofline``: the dominant kernel, the M = 1 step kernel (the whole
+    449-job pass is one launch of it), with its HBM traffic per launch from
+    the committed rocprofv3 counter summary (profiles/), null once the
+    kernel sources differ from those the counters were taken with;
+  * ``cpu_baseline``: the CPU oracle, untuned, on bounded samples of the
+    same workloads on this host's cores.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--ms 1,4,17,68]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--ms 1,4,17,68] [--config all|1|2|3|4]
 """
 from __future__ import annotations
 
@@ -41,7 +43,12 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PASS_WEIGHT_BYTES = 14115962880
+PASS_ELEMENTS = 25095045120
+# cold-cache rotation: distinct weight copies over more than 4x the 256 MB
+# last-level cache
+ROTATE_BYTES = 1 << 30
 
 
 def parse():
@@ -50,6 +57,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ms", default="1,4,17,68")
+    ap.add_argument("--config", default="all", choices=["all", "1", "2", "3", "4"],
+                    help="all: one JSON line with every config; i: that config's line only")
+    ap.add_argument("--reps", type=int, default=200, help="timed launches per single matrix")
+    ap.add_argument("--lm-steps", type=int, default=1000, help="lm_head verify steps per V (config 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     return ap.parse_args()
@@ -70,16 +81,17 @@ def log(msg):
 def time_launches(fn, steps, warmup, per_step=None):
     """Average ms of `fn` (work enqueued on the current stream), timed with
     events recorded on that stream.  With a list `per_step`, an event
-    between consecutive steps also gives each step's ms (appended to it)."""
+    between consecutive steps also gives each step's ms (appended to it).
+    `fn` takes the step index."""
     import torch
-    for _ in range(warmup):
-        fn()
+    for i in range(warmup):
+        fn(i)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step is not None else 2)]
     ev[0].record(s)
     for i in range(steps):
-        fn()
+        fn(i)
         if per_step is not None:
             ev[i + 1].record(s)
     ev[-1].record(s)
@@ -89,14 +101,22 @@ def time_launches(fn, steps, warmup, per_step=None):
     return ev[0].elapsed_time(ev[-1]) / steps
 
 
-def pass_io_bytes(M: int) -> int:
-    """Algorithmic activation and output bytes of one pass of the timed
-    step (257 jobs): 2*M*K of X in and 4*M*N of Y out per GEMM job, and for
-    the lm_head 2*M*K in and 4*(M + S) out (argmax per row, accept length per
-    sequence; S = M/17 sequences of 17 rows for M >= 17, else M)."""
+def percentiles_us(ms_list):
+    q = sorted(ms_list)
+    return [round(q[min(len(q) - 1, int(f * (len(q) - 1) + 0.5))] * 1000, 2) for f in (0.1, 0.5, 0.9)]
+
+
+def pass_io_bytes(M: int, fused: bool) -> int:
+    """Algorithmic activation and output bytes of one pass: 2*M*K of X in
+    and 4*M*N of Y out per GEMM job, and for the lm_head 2*M*K in and
+    4*(M + S) out (argmax per row, accept length per sequence; S = M/17
+    sequences of 17 rows for M >= 17, else M)."""
     from verify_gemm_amd import synth
     h, f = synth.HIDDEN, synth.MLP
-    jobs = [(3 * h, h), (h, h), (2 * f, h), (h, f)]  # q|k|v, o, gate|up, down: (N, K)
+    if fused:
+        jobs = [(3 * h, h), (h, h), (2 * f, h), (h, f)]  # q|k|v, o, gate|up, down: (N, K)
+    else:
+        jobs = [(h, h)] * 4 + [(f, h)] * 2 + [(h, f)]
     layer = sum(2 * M * k + 4 * M * n for n, k in jobs)
     seqs = M // 17 if M >= 17 else M
     return synth.LAYERS * layer + 2 * M * h + 4 * (M + seqs)
@@ -109,45 +129,9 @@ def bwprobe(device, gib=8, reps=10):
     nbytes = gib << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=device)
     sink = torch.empty(binding.bwprobe_sink_floats(), dtype=torch.float32, device=device)
-    ms = time_launches(lambda: binding.bwprobe(buf, sink), reps, 1)
+    ms = time_launches(lambda i: binding.bwprobe(buf, sink), reps, 1)
     del buf
     return nbytes / (ms * 1e-3) / 1e9
-
-
-def blas_threads() -> int:
-    """Threads the oracle's BLAS calls run on (what numpy's library reports)."""
-    try:
-        from threadpoolctl import threadpool_info
-        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
-        if n:
-            return max(n)
-    except Exception:  # noqa: BLE001 - the count is informational
-        pass
-    return len(os.sched_getaffinity(0))
-
-
-def cpu_baseline(weights, budget_s: float = 12.0, max_layers: int = 16):
-    """The CPU oracle, untuned, at M = 1 on whole layers (q, k, v, o, gate,
-    up, down) in order, until about `budget_s` seconds of CPU work."""
-    import numpy as np
-
-    import oracle
-    from verify_gemm_amd import synth
-    rng = np.random.default_rng(5)
-    xs = {k: synth.gen_x(rng, 1, k, 0.1) for k in (synth.HIDDEN, synth.MLP)}
-    nbytes, dt, layers = 0, 0.0, 0
-    while layers < max_layers and dt < budget_s:
-        for m in (m for m in weights.mats if m["layer"] == layers):
-            wq, ws = m["wq"].cpu().numpy(), m["ws"].cpu().numpy()
-            t0 = time.perf_counter()
-            oracle.nvfp4_gemm_ref(xs[m["k"]], wq, ws, m["g"], with_bound=False)
-            dt += time.perf_counter() - t0
-            nbytes += wq.size + ws.size
-        layers += 1
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"layers 0-{layers - 1} (q,k,v,o,gate,up,down; {nbytes} weight bytes) at M=1 through the "
-                      f"fp64 numpy oracle (no error bounds) in {dt:.1f} s of oracle time; a full pass is "
-                      f"{PASS_WEIGHT_BYTES / nbytes:.1f}x this sample (~{dt * PASS_WEIGHT_BYTES / nbytes:.0f} s)"}
 
 
 def recorded_traffic(kernel: str):
@@ -161,6 +145,341 @@ def recorded_traffic(kernel: str):
     return rec["traffic_bytes"].get(kernel)
 
 
+def rate_entry(nbytes, ms, probe, extra_bytes=0):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    e = {"us": round(ms * 1000, 2), "weight_gbps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+         "pct_of_probe": round(100 * gbps / probe, 2)}
+    if extra_bytes:
+        e["total_algorithmic_gbps"] = round((nbytes + extra_bytes) / (ms * 1e-3) / 1e9, 1)
+    return e
+
+
+# --------------------------------------------------------------------------
+# config 4: the full pass
+# --------------------------------------------------------------------------
+def time_pass(run, args, probe, wbytes, M, fused, with_unfused):
+    import torch
+    run.run()
+    torch.cuda.synchronize()
+    if run.check():
+        raise RuntimeError(f"M={M}: a stage wait timed out; the step is invalid")
+    steps_ms = []
+    ms = time_launches(lambda i: run.run(), args.steps, args.warmup, steps_ms)
+    if run.check():
+        raise RuntimeError(f"M={M}: a stage wait timed out during timing")
+    gbps = wbytes / (ms * 1e-3) / 1e9
+    e = {"us_per_pass": round(ms * 1000, 2), "weight_gbps": round(gbps, 1),
+         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "pct_of_probe": round(100 * gbps / probe, 2),
+         "us_p10_p50_p90": percentiles_us(steps_ms),
+         "total_algorithmic_gbps": round((wbytes + pass_io_bytes(M, fused)) / (ms * 1e-3) / 1e9, 1),
+         "jobs": run.step.info()["jobs"],
+         "schedule": "one persistent launch" if M == 1 else "one launch per job"}
+    if M != 1:
+        e["persistent_us_per_pass"] = round(time_launches(lambda i: run.run_persistent(), args.steps,
+                                                          args.warmup) * 1000, 2)
+        if run.check():
+            raise RuntimeError(f"M={M}: a stage wait timed out in the persistent launch")
+    if with_unfused:
+        reps = max(2, min(args.steps, 5))
+        g = run.capture_unfused()
+        e["unfused_graph_us_per_pass"] = round(time_launches(lambda i: g.replay(), reps, 1) * 1000, 1)
+        del g
+    return e
+
+
+def pass_roofline(M, us, probe):
+    """The pass against the HBM roofline (weight bytes over the pass time);
+    at M = 68 also against the bf16 MFMA roofline (2*M flops per weight
+    element, 3.41e12 per pass)."""
+    achieved = PASS_WEIGHT_BYTES / (us * 1e-6) / 1e9
+    r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBPS, 4), "frac_of_probe": round(achieved / probe, 4)}
+    if M >= 17:
+        tflops = 2.0 * M * PASS_ELEMENTS / (us * 1e-6) / 1e12
+        r["mfma"] = {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return r
+
+
+def config4(args, dev, probe):
+    import torch
+
+    from verify_gemm_amd import weightpass
+    t0 = time.time()
+    log("[bench] config 4: generating the 449 NVFP4 matrices on the device")
+    weights = weightpass.PassWeights(dev)
+    wbytes = weights.weight_bytes()
+    assert wbytes == PASS_WEIGHT_BYTES
+    torch.cuda.synchronize()
+    log(f"[bench] weights: {wbytes} bytes in {time.time() - t0:.1f}s")
+    per_m = {}
+    for M in [int(v) for v in args.ms.split(",")]:
+        # the headline: 449 separate jobs in vg_pass_run's schedule for M
+        run = weightpass.PassRun(weights, M)
+        e = time_pass(run, args, probe, wbytes, M, False, not args.no_unfused)
+        run.close()
+        del run
+        # the fused-projection variant (257 jobs), a labelled extra
+        fr = weightpass.PassRun(weights, M, fused=True)
+        f = time_pass(fr, args, probe, wbytes, M, True, not args.no_unfused)
+        f["note"] = ("each layer's q|k|v and gate|up read as one stacked matrix; per-matrix tensor scales "
+                     "kept as per-row scales; outputs bit-identical to the 449-job step")
+        fr.close()
+        del fr
+        e["fused"] = f
+        e["roofline"] = pass_roofline(M, e["us_per_pass"], probe)
+        per_m[str(M)] = e
+        log(f"[bench] M={M}: 449 jobs {e['us_per_pass']} us ({e['pct_hbm_peak']} %), "
+            f"257 jobs {f['us_per_pass']} us ({f['pct_hbm_peak']} %)")
+        torch.cuda.empty_cache()
+    return weights, per_m
+
+
+# --------------------------------------------------------------------------
+# configs 1, 2 and FP8: single matrices over rotating cold copies
+# --------------------------------------------------------------------------
+def rotating_nvfp4(n, k, seed, dev):
+    """Distinct device weight copies of one shape, >= ROTATE_BYTES in all."""
+    from verify_gemm_amd import synth
+    per = n * k // 2 + n * k // 16
+    copies = max(2, -(-ROTATE_BYTES // per))
+    return [synth.gen_weights_device(n, k, seed * 1000 + c, dev) for c in range(copies)], per
+
+
+def time_matrix(fn, copies, args):
+    steps_ms = []
+    ms = time_launches(lambda i: fn(i % copies), args.reps, 10, steps_ms)
+    return ms, percentiles_us(steps_ms)
+
+
+def single_matrices(args, dev, probe):
+    import torch
+
+    from verify_gemm_amd import binding, synth
+    out = {"1": [], "2": []}
+    rng_seed = 1001
+    for cfg, M, shapes, sigma in (("1", 1, [(17408, 5120), (5120, 5120)], 0.1),
+                                  ("2", 17, [(5120, 17408), (17408, 5120)], 1.0)):
+        for n, k in shapes:
+            seed = synth.SEED_BASE + int(cfg)
+            ws_list, per = rotating_nvfp4(n, k, seed * 7 + n + k, dev)
+            x = synth.gen_x_device(M, k, seed * 11 + k, dev, sigma)
+            g = 0.5 + 1.5 * ((n * 31 + k) % 97) / 96.0   # a fixed g in [0.5, 2]
+            y = torch.empty((M, n), dtype=torch.float32, device=dev)
+            io = 2 * M * k + 4 * M * n
+            forms = [("nvfp4_gemm", lambda c: binding.nvfp4_gemm(x, ws_list[c][0], ws_list[c][1], g, y))]
+            wsb = binding.gemm_workspace_bytes(M, n, k)
+            if wsb:
+                work = binding.new_workspace(wsb, dev)
+                forms.append(("nvfp4_gemm_ex", lambda c: binding.nvfp4_gemm(x, ws_list[c][0], ws_list[c][1], g, y,
+                                                                            workspace=work)))
+            for name, fn in forms:
+                ms, pct = time_matrix(fn, len(ws_list), args)
+                e = {"M": M, "N": n, "K": k, "entry": name, **rate_entry(per, ms, probe, io),
+                     "us_p10_p50_p90": pct, "copies": len(ws_list), "rotation_bytes": per * len(ws_list),
+                     "cold": True, "seed": seed}
+                out[cfg].append(e)
+                log(f"[bench] config {cfg} {n}x{k} M={M} {name}: {e['us']} us, {e['weight_gbps']} GB/s")
+            del ws_list
+            torch.cuda.empty_cache()
+    return out
+
+
+def fp8_matrices(args, dev, probe):
+    import torch
+
+    from verify_gemm_amd import binding, synth
+    n, k = 17408, 5120
+    per = n * k
+    copies = max(2, -(-ROTATE_BYTES // per))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.SEED_BASE + 8)
+    # E4M3 bytes: uniform over the finite codes (0x7F / 0xFF, the NaNs, excluded)
+    mats = []
+    for _ in range(copies):
+        b = torch.randint(0, 254, (n, k), dtype=torch.int32, device=dev, generator=gen)
+        b = b + (b >= 0x7F).to(torch.int32)
+        mats.append(b.to(torch.uint8))
+    rs = 0.5 + torch.rand(n, device=dev, generator=gen)
+    out = []
+    for M in (1, 17, 68):
+        x = synth.gen_x_device(M, k, 9000 + M, dev)
+        y = torch.empty((M, n), dtype=torch.float32, device=dev)
+        ms, pct = time_matrix(lambda c: binding.fp8_gemm(x, mats[c], 0.01, row_scale=rs, y=y), copies, args)
+        e = {"M": M, "N": n, "K": k, "entry": "fp8_gemm (per-row scales)",
+             **rate_entry(per, ms, probe, 2 * M * k + 4 * M * n + 4 * n),
+             "us_p10_p50_p90": pct, "copies": copies, "rotation_bytes": per * copies, "cold": True}
+        out.append(e)
+        log(f"[bench] fp8 {n}x{k} M={M}: {e['us']} us, {e['weight_gbps']} GB/s")
+    del mats
+    torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------
+# config 3: lm_head verify over 1000 seeded steps
+# --------------------------------------------------------------------------
+def golden_path(v, steps):
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", f"lmhead_v{v}_s{steps}.npz")
+
+
+def lmhead_steps(args, dev, probe):
+    """M = 17, K = 5120, both head sizes: the weights and the per-step X of
+    the stored 1000-step workload (seeded host generation), the stored
+    drafts, one lmhead_argmax_accept_ex call per step rotating over cold
+    weight copies; the argmax and accept lengths are compared with the
+    stored oracle results on decisive rows / steps, near ties counted."""
+    import numpy as np
+    import torch
+
+    from verify_gemm_amd import binding, synth
+    out = []
+    T = synth.T_VERIFY
+    for v in (synth.VOCAB, synth.VOCAB_SLICE):
+        gp = golden_path(v, 1000)
+        gold = np.load(gp, allow_pickle=False) if os.path.exists(gp) else None
+        steps = args.lm_steps
+        t0 = time.time()
+        wq, ws, g = synth.lmhead_weights(v)
+        xh = synth.lmhead_steps_x(steps, v)
+        per = wq.nbytes + ws.nbytes
+        copies = max(2, -(-ROTATE_BYTES // per))
+        wq_d = torch.from_numpy(wq).to(dev)
+        ws_d = torch.from_numpy(ws).to(dev)
+        wcopies = [(wq_d, ws_d)] + [(wq_d.clone(), ws_d.clone()) for _ in range(copies - 1)]
+        x_d = torch.from_numpy(xh.view(np.int16)).to(dev).view(torch.bfloat16)
+        if gold is not None and steps <= gold["drafts"].shape[0]:
+            drafts = gold["drafts"][:steps]
+        else:
+            drafts = np.random.default_rng(v).integers(0, v, size=(steps, T - 1)).astype(np.int32)
+            gold = None
+        d_d = torch.from_numpy(np.ascontiguousarray(drafts)).to(dev)
+        am = torch.empty((steps, T), dtype=torch.int32, device=dev)
+        al = torch.empty((steps, 1), dtype=torch.int32, device=dev)
+        work = binding.new_workspace(binding.lmhead_workspace_bytes(T), dev)
+        log(f"[bench] config 3 V={v}: inputs in {time.time() - t0:.1f}s, {copies} weight copies")
+
+        def step(i):
+            c = wcopies[i % copies]
+            binding.lmhead_argmax_accept_ex(x_d[i * T:(i + 1) * T], c[0], c[1], g, d_d[i:i + 1], T, work,
+                                            argmax=am[i], accept_len=al[i])
+
+        for i in range(min(steps, 10)):
+            step(i)
+        torch.cuda.synchronize()
+        steps_ms = []
+        ms = time_launches(step, steps, 0, steps_ms)
+        e = {"M": T, "K": synth.HIDDEN, "V": v, "steps": steps, "entry": "lmhead_argmax_accept_ex",
+             **rate_entry(per, ms, probe, 2 * T * synth.HIDDEN + 4 * (T + 1)),
+             "us_p10_p50_p90": percentiles_us(steps_ms), "copies": copies, "cold": True,
+             "seed": synth.SEED_BASE + 3}
+        e["us_per_step"] = e.pop("us")
+        amh, alh = am.cpu().numpy(), al.cpu().numpy()[:, 0]
+        if gold is not None:
+            dec = gold["decisive"][:steps]
+            sdec = gold["step_decisive"][:steps]
+            e["parity"] = {
+                "oracle": os.path.relpath(gp, os.path.dirname(os.path.abspath(__file__))),
+                "decisive_rows": int(dec.sum()), "near_tie_rows": int((~dec).sum()),
+                "argmax_mismatch_on_decisive_rows": int((amh[dec] != gold["argmax"][:steps][dec]).sum()),
+                "decisive_steps": int(sdec.sum()), "near_tie_steps": int((~sdec).sum()),
+                "accept_len_mismatch_on_decisive_steps": int((alh[sdec] != gold["accept_len"][:steps][sdec]).sum()),
+                "mean_accept_len": round(float(alh.mean()), 3)}
+        out.append(e)
+        log(f"[bench] config 3 V={v}: {e['us_per_step']} us per step, {e['weight_gbps']} GB/s, "
+            f"parity {e.get('parity')}")
+        del wcopies, wq_d, ws_d, x_d
+        torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------
+# CPU oracle timings
+# --------------------------------------------------------------------------
+def blas_threads() -> int:
+    """Threads the oracle's BLAS calls run on (what numpy's library reports)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:  # noqa: BLE001 - the count is informational
+        pass
+    return 1
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_bits(t):
+    import numpy as np
+    return t.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+def cpu_baseline(weights, ms_list, budget_per_m: float = 3.0):
+    """The CPU oracle, untuned, on this host.  Per M: whole layers (q, k, v,
+    o, gate, up, down) of the pass's own weights and an X of the pass's
+    shapes, until about `budget_per_m` seconds of oracle time.  Config 1/2
+    single matrices (dequant + fp64 GEMM) and the lm_head verify of the
+    65,536-row head over a batch of steps, amortised per step."""
+    import numpy as np
+
+    import oracle
+    from verify_gemm_amd import synth
+    per_m = {}
+    for M in ms_list:
+        rng = np.random.default_rng(5 + M)
+        xs = {k: synth.gen_x(rng, M, k) for k in (synth.HIDDEN, synth.MLP)}
+        nbytes, dt, layers = 0, 0.0, 0
+        while layers < synth.LAYERS and dt < budget_per_m:
+            for m in (m for m in weights.mats if m["layer"] == layers):
+                wq, ws = m["wq"].cpu().numpy(), m["ws"].cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.nvfp4_gemm_ref(xs[m["k"]], wq, ws, m["g"], with_bound=False)
+                dt += time.perf_counter() - t0
+                nbytes += wq.size + ws.size
+            layers += 1
+        per_m[str(M)] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s",
+                         "sample": f"layers 0-{layers - 1}, {nbytes} weight bytes in {dt:.2f} s",
+                         "full_pass_s_extrapolated": round(dt * PASS_WEIGHT_BYTES / nbytes, 1)}
+    mats = []
+    for cfg, M, n, k in (("1", 1, 17408, 5120), ("1", 1, 5120, 5120), ("2", 17, 5120, 17408),
+                         ("2", 17, 17408, 5120)):
+        c = synth.decode_gemv(n, k) if M == 1 else synth.verify_gemm(n, k)
+        t0 = time.perf_counter()
+        oracle.nvfp4_gemm_ref(c["x"], c["wq"], c["ws"], c["g"], with_bound=False)
+        dt = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        oracle.nvfp4_gemm_ref(c["x"], c["wq"], c["ws"], c["g"])
+        dtb = time.perf_counter() - t1
+        mats.append({"config": cfg, "M": M, "N": n, "K": k, "ms": round(dt * 1000, 1),
+                     "ms_with_bound": round(dtb * 1000, 1),
+                     "weight_gbps": round((c["wq"].nbytes + c["ws"].nbytes) / dt / 1e9, 4)})
+    v, nsteps = synth.VOCAB_SLICE, 40
+    wq, ws, g = synth.lmhead_weights(v)
+    x = synth.lmhead_steps_x(nsteps, v)
+    t0 = time.perf_counter()
+    oracle.lmhead_ref(x, wq, ws, g, T=synth.T_VERIFY)
+    dt = time.perf_counter() - t0
+    lm = {"V": v, "steps": nsteps, "s": round(dt, 2), "ms_per_step_amortised": round(dt / nsteps * 1000, 1),
+          "note": "one dequant of the head, then all steps' rows in one fp64 GEMM with bounds"}
+    m1 = per_m[str(ms_list[0])]
+    return {"value": m1["value"], "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"M={ms_list[0]}: {m1['sample']} of the full pass through the fp64 numpy oracle "
+                      f"(no error bounds); a full pass extrapolates to ~{m1['full_pass_s_extrapolated']} s",
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "threads_note": "dequantisation runs in numpy on one thread; the fp64 GEMM on the BLAS threads",
+            "per_m": per_m, "single_matrices": mats, "lmhead": lm}
+
+
+# --------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
@@ -169,109 +488,63 @@ def main():
         sys.exit(2)
     import torch
 
-    from verify_gemm_amd import binding, weightpass
+    from verify_gemm_amd import binding
     binding.load()
     dev = torch.device("cuda:0")
-    t_start = time.time()
-    log("[bench] generating the 449 NVFP4 matrices on the device")
-    weights = weightpass.PassWeights(dev)
-    wbytes = weights.weight_bytes()
-    torch.cuda.synchronize()
-    log(f"[bench] weights: {wbytes} bytes in {time.time() - t_start:.1f}s")
     probe = bwprobe(dev)
     log(f"[bench] bwprobe read ceiling {probe:.0f} GB/s")
     ms_list = [int(v) for v in args.ms.split(",")]
-    per_m = {}
-    for M in ms_list:
-        # The timed step: every layer's {q,k,v} and {gate,up} read as one
-        # stacked matrix each (257 jobs), each member keeping its own tensor
-        # scale as per-row scales -- the same bytes and the same output bits
-        # as 449 separate jobs -- in vg_pass_run's schedule for this M.
-        run = weightpass.PassRun(weights, M, fused=True)
-        run.run()
-        torch.cuda.synchronize()
-        if run.check():
-            raise RuntimeError(f"M={M}: a stage wait timed out; the step is invalid")
-        steps_ms = []
-        ms = time_launches(run.run, args.steps, args.warmup, steps_ms)
-        if run.check():
-            raise RuntimeError(f"M={M}: a stage wait timed out during timing")
-        gbps = wbytes / (ms * 1e-3) / 1e9
-        q = sorted(steps_ms)
-        pct = lambda f: round(q[min(len(q) - 1, int(f * (len(q) - 1) + 0.5))] * 1000, 2)  # noqa: E731
-        entry = {"us_per_pass": round(ms * 1000, 2), "weight_gbps": round(gbps, 1),
-                 "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-                 "pct_of_probe": round(100 * gbps / probe, 2),
-                 "us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
-                 "total_algorithmic_gbps": round((wbytes + pass_io_bytes(M)) / (ms * 1e-3) / 1e9, 1),
-                 "jobs": run.step.info()["jobs"],
-                 "schedule": "one persistent launch" if M == 1 else "one launch per job"}
-        if M != 1:
-            entry["persistent_us_per_pass"] = round(time_launches(run.run_persistent, args.steps, args.warmup) * 1000, 2)
-            if run.check():
-                raise RuntimeError(f"M={M}: a stage wait timed out in the persistent launch")
-        if not args.no_unfused:
-            reps = max(2, min(args.steps, 5))
-            g = run.capture_unfused()
-            entry["unfused_graph_us_per_pass"] = round(time_launches(g.replay, reps, 1) * 1000, 1)
-            del g
-            # the same step as 449 separate jobs, as one launch and as one
-            # launch per job
-            sr = weightpass.PassRun(weights, M)
-            sr.run()
-            torch.cuda.synchronize()
-            if sr.check():
-                raise RuntimeError(f"M={M}: a stage wait timed out in the 449-job step")
-            sep = time_launches(sr.run, reps, 1)
-            gs = sr.capture_unfused()
-            entry["separate_jobs"] = {"jobs": sr.step.info()["jobs"], "us_per_pass": round(sep * 1000, 2),
-                                      "unfused_graph_us_per_pass": round(time_launches(gs.replay, reps, 1) * 1000, 1)}
-            del gs
-            sr.close()
-            del sr
-        per_m[str(M)] = entry
-        log(f"[bench] M={M}: {entry}")
-        run.close()
-        del run
-        torch.cuda.empty_cache()
+    base = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None,
+            "dtype": "e2m1/e4m3 weights x bf16 activations, fp32 accumulation",
+            "data": "synthetic (seeded RNG; codes uniform, scales 2^u, g in [0.5, 2])"}
+    if args.config in ("1", "2", "3"):
+        res = lmhead_steps(args, dev, probe) if args.config == "3" else single_matrices(args, dev, probe)[args.config]
+        first = res[0]
+        line = {"metric": f"config {args.config}: µs and effective weight GB/s per matrix", **base,
+                "value": first["weight_gbps"], "unit": "GB/s",
+                "ms_per_step": round(first.get("us", first.get("us_per_step", 0.0)) / 1000, 5),
+                "config": {"workload": f"config {args.config}", "entries": res}, "bwprobe_read_gbps": round(probe, 1)}
+        print(json.dumps(line), flush=True)
+        return
+    weights, per_m = config4(args, dev, probe)
     head = per_m[str(ms_list[0])]
     kus = head["us_per_pass"]
-    # the roofline is that of one launch of the whole step: at M >= 2 the
-    # persistent launch timed beside the per-job schedule
+    # the dominant kernel: at M = 1 the step kernel, the whole pass in one
+    # launch; at M >= 2 the persistent launch timed beside the per-job schedule
     lus = head.get("persistent_us_per_pass", kus)
-    achieved = wbytes / (lus * 1e-6) / 1e9
+    achieved = PASS_WEIGHT_BYTES / (lus * 1e-6) / 1e9
     out = {
         "metric": "µs per full weight pass + effective weight GB/s (% HBM peak) at M=1/17/68",
         "value": head["weight_gbps"],
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        **{k: base[k] for k in ("n_gpus", "steps", "warmup")},
         "ms_per_step": round(kus / 1000, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "e2m1/e4m3 weights x bf16 activations, fp32 accumulation",
-        "data": "synthetic (seeded device RNG, codes uniform, scales 2^u)",
+        **{k: base[k] for k in ("higher_is_better", "scaling", "vs_baseline", "dtype", "data")},
         "config": {"workload": "full synthetic weight pass: 64 layers x {q,k,v,o 5120x5120; gate,up "
                                "17408x5120; down 5120x17408} + lm_head 248320x5120 with argmax/accept "
-                               f"(449 NVFP4 matrices, {wbytes} weight bytes), one persistent launch per pass at "
-                               "M=1 (one launch per job at M>=2); "
-                               "each layer's q|k|v and gate|up read as one stacked matrix (257 jobs, per-matrix "
-                               "tensor scales kept as per-row scales, outputs bit-identical to 449 jobs)",
-                   "M": ms_list[0], "M_reported": ms_list},
+                               f"(449 NVFP4 matrices as 449 jobs, {PASS_WEIGHT_BYTES} weight bytes), one "
+                               "persistent launch per pass at M=1 (one launch per job at M>=2); the fused "
+                               "257-job step in per_m[M].fused",
+                   "M": ms_list[0], "M_reported": ms_list, "seed": 1004},
         "per_m": per_m,
         "bwprobe_read_gbps": round(probe, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic(step_kernel_name(ms_list[0])),
-                     "kernel": (f"{step_kernel_name(ms_list[0])} (the whole step is one launch of it) "
+                     "kernel": (f"{step_kernel_name(ms_list[0])} (the whole 449-job step is one launch of it) "
                                 f"at M={ms_list[0]}"),
-                     "avg_us": lus, "bytes_per_launch": wbytes},
+                     "avg_us": lus, "bytes_per_launch": PASS_WEIGHT_BYTES},
     }
+    if args.config == "all":
+        out["configs"] = single_matrices(args, dev, probe)
+        out["configs"]["3"] = lmhead_steps(args, dev, probe)
+        out["configs"]["fp8"] = fp8_matrices(args, dev, probe)
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on layer 0 (bounded sample)")
-        out["cpu_baseline"] = cpu_baseline(weights)
+        log("[bench] timing the CPU oracle on bounded samples")
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(weights, ms_list)
+        log(f"[bench] CPU oracle legs: {time.time() - t0:.1f}s")
     print(json.dumps(out), flush=True)
 
 
