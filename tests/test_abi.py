@@ -17,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 VG_OK, VG_ERR_NULL, VG_ERR_SHAPE, VG_ERR_UNSUPPORTED = 0, -1, -2, -3
 VG_ERR_HIP, VG_ERR_WORKSPACE, VG_ERR_ALIGN, VG_ERR_FLAGS = -4, -5, -6, -7
+VG_ERR_SCRATCH = -8
 
 
 @pytest.fixture(scope="module")
@@ -47,7 +48,7 @@ def test_exports_every_header_symbol(lib):
 
 def test_status_strings(lib):
     for code in (VG_OK, VG_ERR_NULL, VG_ERR_SHAPE, VG_ERR_UNSUPPORTED, VG_ERR_HIP, VG_ERR_WORKSPACE,
-                 VG_ERR_ALIGN):
+                 VG_ERR_ALIGN, VG_ERR_FLAGS, VG_ERR_SCRATCH):
         assert binding.status_string(code) != "unknown status"
     assert binding.status_string(12345) == "unknown status"
 
@@ -89,6 +90,24 @@ def test_gemm_ex_workspace_contract(lib, buf):
     assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 17408, p, p + 4, need, None) == VG_ERR_ALIGN
     # validation still applies to the _ex form
     assert lib.nvfp4_gemm_ex(p, p, p, 1.0, 17, 5120, 24, p, None, 0, None) == VG_ERR_SHAPE
+
+
+def test_noalloc_validation(lib, buf):
+    """nvfp4_gemm_noalloc checks its arguments as nvfp4_gemm does, before any
+    HIP call; the largest slice workspace any M <= 68 shape needs on a
+    256-CU device fits its 16 MiB static scratch."""
+    _, p = buf
+    for x, wq, ws, y in [(None, p, p, p), (p, None, p, p), (p, p, None, p), (p, p, p, None)]:
+        assert lib.nvfp4_gemm_noalloc(x, wq, ws, 1.0, 17, 5120, 5120, y, None) == VG_ERR_NULL
+    for m, n, k, code in [(0, 16, 16, VG_ERR_SHAPE), (1, 0, 16, VG_ERR_SHAPE), (1, 16, 24, VG_ERR_SHAPE),
+                          (69, 16, 16, VG_ERR_UNSUPPORTED)]:
+        assert lib.nvfp4_gemm_noalloc(p, p, p, 1.0, m, n, k, p, None) == code
+    for x, wq, ws in [(p + 2, p, p), (p, p + 4, p), (p, p, p + 1)]:
+        assert lib.nvfp4_gemm_noalloc(x, wq, ws, 1.0, 17, 5120, 5120, p, None) == VG_ERR_ALIGN
+    # the most slices a shape can have: fewer 64-row blocks than CUs, three
+    # K slices each
+    worst = max(lib.vg_gemm_workspace_bytes(68, 64 * nb, 17408) for nb in (1, 80, 255))
+    assert 0 < worst <= 16 << 20
 
 
 def test_workspace_sizes(lib):

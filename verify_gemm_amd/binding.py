@@ -50,6 +50,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "nvfp4_gemm": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp]),
         "nvfp4_gemm_ex": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp, sz, vp]),
         "vg_gemm_workspace_bytes": (sz, [i32, i32, i32]),
+        "nvfp4_gemm_noalloc": (i32, [vp, vp, vp, f32, i32, i32, i32, vp, vp]),
         "lmhead_argmax_accept": (i32, [vp, vp, vp, vp, i32, i32, vp, vp, vp]),
         "lmhead_argmax_accept_ex": (i32, [vp, vp, vp, f32, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
         "vg_lmhead_workspace_bytes": (sz, [i32]),
@@ -179,6 +180,23 @@ def nvfp4_gemm(x, wq, ws, gscale: float, y=None, *, workspace=None, invariant=Fa
         st = lib.nvfp4_gemm_ex(px, wq.data_ptr(), ws.data_ptr(), float(gscale), m, n, k, py,
                                pw, workspace.numel(), sp)
     _check(st, "nvfp4_gemm")
+    return y
+
+
+def nvfp4_gemm_noalloc(x, wq, ws, gscale: float, y, *, stream=None):
+    """nvfp4_gemm_noalloc: the workspace form with the library's static
+    per-GPU scratch (no allocation anywhere; ``y`` must be given)."""
+    torch = _torch()
+    lib = load()
+    px = _need(x, torch.bfloat16, 2, "X")
+    m, k = x.shape
+    n = _check_weights(wq, ws, k)
+    py = _need(y, torch.float32, 2, "Y")
+    if tuple(y.shape) != (m, n):
+        raise ValueError("Y must be [M][N]")
+    st = lib.nvfp4_gemm_noalloc(px, wq.data_ptr(), ws.data_ptr(), float(gscale), m, n, k, py,
+                                _stream_ptr(stream))
+    _check(st, "nvfp4_gemm_noalloc")
     return y
 
 

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvgemm.so")
-SOURCES = (["api.cpp", "stream.hip", "step_gemv.hip", "bwprobe.hip"]
+SOURCES = (["api.cpp", "stream.hip", "step_gemv.hip", "bwprobe.hip", "noalloc.hip"]
            + [f"stream_mt{mt}_f{fmt}.hip" for mt in range(6) for fmt in range(2)])
 ARCH = "gfx950"
 
