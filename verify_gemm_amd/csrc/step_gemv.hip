@@ -269,19 +269,55 @@ __device__ __forceinline__ void issue(const StreamJob& j, const Chunk& ch, int w
   }
 }
 
-// The dot products of G slots are computed as 4*G independent four-deep
-// v_dot2 chains -- one per slot and code word -- interleaved in program
-// order: for each code byte, first the G decodes, then the G dot2s into
-// different chains.  A dependent dot2 then comes 4*G instructions after the
-// previous one on its chain, which hides the decode and dot2 latencies
-// inside one wave; a chain-at-a-time order runs at about a third of the
-// issue rate.  Slot g uses code pieces q[S0 + g * SS] of the buffer and
-// activation set x[XI(g)].  Words 0/1 belong to the piece's first
-// 16-element block, words 2/3 to its second; each block's two chains are
-// added and scaled once.
-template <int G, int S0, int SS, int NX>
+// The dot products of G slots.  Slot g uses code pieces q[S0 + g * SS] of
+// the buffer and activation set x[XI(g)]; words 0/1 of a piece belong to
+// its first 16-element block, words 2/3 to its second, and each block's sum
+// is scaled once.  The chains are interleaved in program order (for each
+// code byte, first the decodes, then the dot2s into different chains), so
+// a dependent dot2 comes several instructions after the previous one on
+// its chain and the decode and dot2 latencies hide inside one wave; a
+// chain-at-a-time order runs at about a third of the issue rate.
+//   * BLK (two or three rows per half-wave): one eight-deep chain per
+//     16-element block, 2*G chains, started from zero once per block and
+//     applied with one FMA -- the fewest instructions per code;
+//   * otherwise (one row): 4*G four-deep chains, one per code word, two
+//     added per block, so that even one slot keeps four chains in flight.
+template <int G, int S0, int SS, int NX, bool BLK>
 __device__ __forceinline__ void piece_group(const Buf& b, const u32x4 (&x)[NX][4], const f32x2 (&s)[G],
                                             float (&acc)[G]) {
+  if constexpr (BLK) {
+    float ch[G][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sel = j & 3, half = j >> 2;  // word 2 * blk + half, byte sel
+      bf16x2 e[G][2];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const unsigned word = b.q[S0 + g * SS][2 * blk + half];
+          switch (sel) {
+            case 0: e[g][blk] = e2m1x2_bf16<0>(word); break;
+            case 1: e[g][blk] = e2m1x2_bf16<1>(word); break;
+            case 2: e[g][blk] = e2m1x2_bf16<2>(word); break;
+            default: e[g][blk] = e2m1x2_bf16<3>(word); break;
+          }
+        }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const unsigned xv = x[NX == 1 ? 0 : g][2 * blk + half][sel];
+          ch[g][blk] = __builtin_amdgcn_fdot2_f32_bf16(e[g][blk], as_bf16x2(xv), j == 0 ? 0.0f : ch[g][blk], false);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      acc[g] = __builtin_fmaf(s[g][0], ch[g][0], acc[g]);
+      acc[g] = __builtin_fmaf(s[g][1], ch[g][1], acc[g]);
+    }
+    return;
+  }
   float ch[G][4];
 #pragma unroll
   for (int sel = 0; sel < 4; ++sel) {
@@ -363,7 +399,7 @@ __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch,
         f32x2 s[RH];
 #pragma unroll
         for (int i = 0; i < RH; ++i) s[i] = scale(c, i);
-        piece_group<RH, c * RH, 1, 1>(b, xb[c & 1], s, acc);
+        piece_group<RH, c * RH, 1, 1, true>(b, xb[c & 1], s, acc);
       }
       // keep later pieces' reads from being hoisted into this one (they
       // would all be hoisted to the top and spilled)
@@ -377,7 +413,7 @@ __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch,
       if (c < cpl) {
         if (c + 1 < CMAX && c + 1 < cpl) xpiece(c + 1, xb[(c + 1) & 1][0]);
         const f32x2 s[1] = {scale(c, 0)};
-        piece_group<1, c, 1, 1>(b, xb[c & 1], s, acc);
+        piece_group<1, c, 1, 1, false>(b, xb[c & 1], s, acc);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
