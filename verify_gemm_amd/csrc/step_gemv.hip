@@ -775,12 +775,20 @@ __global__ __launch_bounds__(kWG) void step_gemv_kernel(StreamArgs a) {
   float best_v = -__builtin_inff();
   int best_i = -1;
   const int role = threadIdx.x >> 6;
-  if (role == kIO)
+  // The I/O and store waves share SIMDs with compute waves; their hand-offs
+  // (polls, releases, result stores) are on every chunk's critical path, so
+  // they issue first (measured: the pass 1.2 % faster).
+  if (role == kIO) {
+    __builtin_amdgcn_s_setprio(3);
     io_loop(a, sh, njobs);
-  else if (role == kST)
+    __builtin_amdgcn_s_setprio(0);
+  } else if (role == kST) {
+    __builtin_amdgcn_s_setprio(3);
     store_loop(a, sh, njobs);
-  else
+    __builtin_amdgcn_s_setprio(0);
+  } else {
     compute_loop(a, sh, njobs, best_v, best_i);
+  }
 
   // A launch that waits on stages or has an lm_head counts its workgroups
   // out; the last one finishes the lm_head and zeroes the control block and
