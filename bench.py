@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--lm-steps", type=int, default=1000, help="lm_head verify steps per V (config 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="time only the 449-job step (profiles then see one kind of pass launch)")
     return ap.parse_args()
 
 
@@ -219,18 +221,20 @@ def config4(args, dev, probe):
         e = time_pass(run, args, probe, wbytes, M, False, not args.no_unfused)
         run.close()
         del run
-        # the fused-projection variant (257 jobs), a labelled extra
-        fr = weightpass.PassRun(weights, M, fused=True)
-        f = time_pass(fr, args, probe, wbytes, M, True, not args.no_unfused)
-        f["note"] = ("each layer's q|k|v and gate|up read as one stacked matrix; per-matrix tensor scales "
-                     "kept as per-row scales; outputs bit-identical to the 449-job step")
-        fr.close()
-        del fr
-        e["fused"] = f
         e["roofline"] = pass_roofline(M, e["us_per_pass"], probe)
+        msg = f"[bench] M={M}: 449 jobs {e['us_per_pass']} us ({e['pct_hbm_peak']} %)"
+        if not args.no_fused:
+            # the fused-projection variant (257 jobs), a labelled extra
+            fr = weightpass.PassRun(weights, M, fused=True)
+            f = time_pass(fr, args, probe, wbytes, M, True, not args.no_unfused)
+            f["note"] = ("each layer's q|k|v and gate|up read as one stacked matrix; per-matrix tensor scales "
+                         "kept as per-row scales; outputs bit-identical to the 449-job step")
+            fr.close()
+            del fr
+            e["fused"] = f
+            msg += f", 257 jobs {f['us_per_pass']} us ({f['pct_hbm_peak']} %)"
         per_m[str(M)] = e
-        log(f"[bench] M={M}: 449 jobs {e['us_per_pass']} us ({e['pct_hbm_peak']} %), "
-            f"257 jobs {f['us_per_pass']} us ({f['pct_hbm_peak']} %)")
+        log(msg)
         torch.cuda.empty_cache()
     return weights, per_m
 

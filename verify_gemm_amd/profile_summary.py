@@ -20,6 +20,12 @@ produced its input:
     python -m verify_gemm_amd.profile_summary trace STATS_CSV CMD OUT
     python -m verify_gemm_amd.profile_summary pmc FETCH_CSV WRITE_CSV CMD_F CMD_W PROBE_BYTES FILL_BYTES OUT
     python -m verify_gemm_amd.profile_summary busy COUNTER_CSV CMD OUT
+    python -m verify_gemm_amd.profile_summary counters TITLE OUT CMD1 CSV1 [CMD2 CSV2 ...]
+
+  * ``counters``: per-dispatch averages of every counter of one or more
+    counter runs (one run per group of counters the hardware can collect
+    together), per kernel, each shown also per SQ_BUSY_CYCLES x 32 SIMDs
+    where the run has SQ_BUSY_CYCLES.
 """
 from __future__ import annotations
 
@@ -101,11 +107,12 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
             continue
         lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    lines += ["", "stream_kernel<MT, MODE, FMT, ANYK>: MT 16-row M-tiles (2 at M = 17, 5 at M = 68), MODE 0 "
-              "one GEMM job, 1 the lm_head, 2 the whole pass as one persistent launch; FMT 0 NVFP4; ANYK 0 "
-              "when every K is a multiple of 128.  A launch of step_gemv_kernel (M = 1) or of a MODE 2 "
-              f"kernel is one whole pass.  At M >= 2 the step's default schedule is one launch per job: "
-              f"{GEMM_JOBS_PER_PASS} GEMM launches of MODE 0 and one lm_head launch of MODE 1 per pass.", ""]
+    lines += ["", "stream_kernel<MT, MODE, FMT, ANYK>: MT 16-row M-tiles (1 at M = 4, 2 at M = 17, 5 at M = 68), "
+              "MODE 0 one GEMM job, 1 the lm_head, 2 the whole pass as one persistent launch; FMT 0 NVFP4; ANYK 0 "
+              "when every K is a multiple of 128.  A launch of step_gemv_kernel (M = 1) or of a MODE 2 kernel is one "
+              "whole pass; vg_pass_run takes the MODE 2 launch at M >= 2 when a stage holds several jobs (the 449-job "
+              f"step) and MODE 0 / 1 launches otherwise (the fused step: {GEMM_JOBS_PER_PASS} GEMM launches and one "
+              "lm_head launch per pass).", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
 
@@ -208,6 +215,37 @@ def busy(csv_path: str, cmd: str, out: str) -> None:
         f.write("\n".join(lines))
 
 
+def counters(title: str, out: str, runs) -> None:
+    """Per-kernel, per-dispatch averages of the counters of several runs."""
+    lines = [f"# {title}", "", "Counter runs (run from /tmp, `TMPDIR=/tmp`), one per group of counters the "
+             "hardware collects together:", "", "```"] + [cmd for cmd, _ in runs] + ["```", ""]
+    for cmd, path in runs:
+        names = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] not in names:
+                names.append(r["Counter_Name"])
+        vals = {c: _per_dispatch(path, c) for c in names}
+        kernels = sorted({k for c in names for k in vals[c][0] if k.startswith(("stream_kernel", "step_gemv"))})
+        busy = vals.get("SQ_BUSY_CYCLES", ({}, {}))[0]
+        lines += ["| kernel | dispatches | " + " | ".join(names) + " |",
+                  "|---|---:|" + "---:|" * len(names)]
+        for k in kernels:
+            cells = []
+            for c in names:
+                v = vals[c][0].get(k, 0.0)
+                den = busy.get(k, 0.0) * SIMDS_PER_SE
+                rel = f" ({100 * v / den:.1f} %)" if den and c.startswith("SQ_") and c != "SQ_BUSY_CYCLES" else ""
+                cells.append(f"{v:.4g}{rel}")
+            lines.append(f"| {k} | {vals[names[0]][1].get(k, 0)} | " + " | ".join(cells) + " |")
+        lines.append("")
+    lines += ["Per dispatch, averaged.  A percentage is the counter over SQ_BUSY_CYCLES x "
+              f"{SIMDS_PER_SE} (the SQ counters sum over SIMDs, SQ_BUSY_CYCLES over shader engines): a "
+              "share of the SIMD cycles while the kernel runs.  TA and TCP counters are sums over their "
+              "units (the _sum forms).", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+
+
 def recorded_traffic(path: str):
     """The traffic record of a pmc summary, or None if the summary is
     missing or the kernel sources changed since it was taken."""
@@ -232,6 +270,8 @@ def main(argv):
         pmc(argv[2], argv[3], argv[4], argv[5], int(argv[6]), int(argv[7]), argv[8])
     elif argv[1] == "busy":
         busy(argv[2], argv[3], argv[4])
+    elif argv[1] == "counters":
+        counters(argv[2], argv[3], list(zip(argv[4::2], argv[5::2])))
     else:
         raise SystemExit(__doc__)
 
