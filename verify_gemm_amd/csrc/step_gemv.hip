@@ -151,9 +151,12 @@ __device__ __forceinline__ void lds_store(unsigned* p, unsigned v) {
 
 
 __host__ __device__ __forceinline__ int pieces_per_lane(int k) { return (k + 1023) >> 10; }
+// min(kSlots / pieces, kMaxRH) without a division (this runs per job in
+// every wave's chunk walk).
 __host__ __device__ __forceinline__ int rows_per_half(int k) {
-  const int r = kSlots / pieces_per_lane(k);
-  return r < kMaxRH ? r : kMaxRH;
+  static_assert(kSlots == 18 && kMaxRH == 3, "the thresholds below are 18 / pieces, capped at 3");
+  const int cpl = pieces_per_lane(k);
+  return cpl <= 6 ? 3 : (cpl <= 9 ? 2 : 1);
 }
 __host__ __device__ __forceinline__ int chunk_cap(int k) { return 2 * kCW * rows_per_half(k); }
 
@@ -208,25 +211,64 @@ __device__ __forceinline__ void wave_rows(int rows, int w, int& begin, int& coun
   count = rows * (w + 1) / kCW - begin;
 }
 
+// Rows per half-wave that a wave's slots are laid out for in one chunk:
+// enough for its `count` rows, at most what the job's K allows.  A wave
+// computes every row slot of its layout (slots past its rows hold zero
+// codes), so a wave with 3 or 4 rows of a 20-row chunk lays out 2 per
+// half-wave, not the 3 that K = 5120 allows (measured: those chunks
+// computed 6 rows per wave for 3 or 4 real ones).
+__device__ __forceinline__ int wave_rh(int k, int count) {
+  const int r = (count + 1) >> 1, m = rows_per_half(k);
+  return r < m ? (r > 0 ? r : 1) : m;
+}
+
 // Walks this workgroup's chunks in job order (the same in every wave).
+// The chunk walk runs in every wave between chunks, so it avoids runtime
+// divisions (software sequences on this GPU): the workgroup's rows come
+// from a shift when the grid is a power of two, a job's chunk count from a
+// constant divisor, and the chunk sizes from one quotient and remainder
+// per job.
 struct Cursor {
-  int job = 0, pos = 0, end = 0, left = 0;  // left: chunks still to cut from [pos, end)
+  int job = 0, pos = 0, left = 0;  // left: chunks still to cut, from row pos on
+  int idx = 0, base = 0, rem = 0;  // chunk ordinal in the job; the first rem chunks have base + 1 rows, the rest base
 };
 
+// Rows [pos, end) of a job with n rows belong to this workgroup: an even
+// split over the grid, floor(n * w / G) .. floor(n * (w + 1) / G).
+__device__ __forceinline__ void job_rows(int n, int& pos, int& end) {
+  const unsigned G = gridDim.x, w = blockIdx.x;
+  if ((G & (G - 1)) == 0 && G <= 1024 && n <= (1 << 21)) {  // n * G < 2^32
+    const int s = __builtin_ctz(G);
+    pos = (int)(((unsigned)n * w) >> s);
+    end = (int)(((unsigned)n * (w + 1)) >> s);
+  } else {
+    pos = (int)((long long)n * w / G);
+    end = (int)((long long)n * (w + 1) / G);
+  }
+}
+
 __device__ __forceinline__ bool next_chunk(const Shared& sh, int njobs, Cursor& cu, Chunk& out) {
+  static_assert(2 * kCW == 12, "chunk caps below are 12 * rows_per_half");
   while (cu.left == 0) {
     if (cu.job >= njobs) return false;
     const StreamJob j = lds_job(sh, cu.job);
-    const long long G = gridDim.x, w = blockIdx.x;
-    cu.pos = (int)(j.n * w / G);
-    cu.end = (int)(j.n * (w + 1) / G);
-    const int cap = chunk_cap(j.k);
-    cu.left = (cu.end - cu.pos + cap - 1) / cap;
+    int end;
+    job_rows(j.n, cu.pos, end);
+    const int rows = end - cu.pos;
+    // chunks of at most chunk_cap(k) rows, as equal as rows allow: the
+    // first rows % cnt of them one row larger
+    const int rh = rows_per_half(j.k);
+    const int cnt = rh == 3 ? (rows + 35) / 36 : rh == 2 ? (rows + 23) / 24 : (rows + 11) / 12;
+    cu.left = cnt;
+    cu.idx = 0;
+    cu.base = cnt > 0 ? rows / cnt : 0;
+    cu.rem = rows - cu.base * cnt;
     if (cu.left == 0) ++cu.job;
   }
-  const int rows = (cu.end - cu.pos + cu.left - 1) / cu.left;  // near-equal chunks
+  const int rows = cu.base + (cu.idx < cu.rem ? 1 : 0);
   out = Chunk{cu.job, cu.pos, rows};
   cu.pos += rows;
+  ++cu.idx;
   if (--cu.left == 0) ++cu.job;
   return true;
 }
@@ -248,13 +290,14 @@ struct Epoch {
 
 // ---- compute waves -----------------------------------------------------
 
-// Slot s of the buffer holds piece c = s / rh of local row 2 * (s % rh) + h.
+// Slot s of the buffer holds piece c = s / rh of local row 2 * (s % rh) + h,
+// rh = wave_rh(K, the wave's rows of the chunk).
 __device__ __forceinline__ void issue(const StreamJob& j, const Chunk& ch, int w, Buf& b) {
   const int lane = threadIdx.x & 63, h = lane >> 5, L = lane & 31;
   int wb, wc;
   wave_rows(ch.rows, w, wb, wc);
   const unsigned rb = (unsigned)j.k >> 1;
-  const int cpl = pieces_per_lane(j.k), rh = rows_per_half(j.k);
+  const int cpl = pieces_per_lane(j.k), rh = wave_rh(j.k, wc);
   const size_t row0 = (size_t)(ch.r0 + wb);
   const __amdgpu_buffer_rsrc_t rw = rsrc(j.wq + row0 * rb, (unsigned)wc * rb);
   int i = 0, c = 0;
@@ -349,7 +392,7 @@ __device__ __forceinline__ void piece_group(const Buf& b, const u32x4 (&x)[NX][4
 }
 
 // Row sums times g for the wave's rows of a chunk whose rows take RH slots
-// per half-wave (RH = 18 / cpl).  Slots of rows the wave does not have hold
+// per half-wave (RH = wave_rh: at most 18 / cpl).  Slots of rows the wave does not have hold
 // zero codes (their loads were out of range) and their sums are never
 // used.  The rows of one piece form one group (one row: the piece alone);
 // pieces c >= cpl are skipped (uniformly).  Results go to LDS (GEMM) or
@@ -440,8 +483,10 @@ __device__ __forceinline__ void compute_cls(const StreamJob& j, const Chunk& ch,
 __device__ __forceinline__ void compute(const StreamJob& j, const Chunk& ch, int w, const Buf& b,
                                         const unsigned short* sc, float* res, const u32x4* xs,
                                         float& best_v, int& best_i) {
-  static_assert(kMaxRH == 3, "the classes below are the values of rows_per_half");
-  switch (rows_per_half(j.k)) {
+  static_assert(kMaxRH == 3, "the classes below are the values of wave_rh");
+  int wb, wc;
+  wave_rows(ch.rows, w, wb, wc);
+  switch (wave_rh(j.k, wc)) {
     case 3: compute_cls<3>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
     case 2: compute_cls<2>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
     default: compute_cls<1>(j, ch, w, b, sc, res, xs, best_v, best_i); break;
