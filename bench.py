@@ -4,7 +4,7 @@ One step = one pass over the whole hot path: 64 layers x {q, k, v, o, gate,
 up, down} NVFP4 GEMMs + the lm_head with fused argmax and greedy accept
 (449 matrices, 14,115,962,880 weight bytes), run by the native step
 executor (vg_pass_run) in its faster schedule: ONE persistent kernel launch
-at M = 1, one launch per job at M >= 2.  Reported at M = 1 (plain decode),
+at M = 1, one launch per dependency stage at M >= 2.  Reported at M = 1 (plain decode),
 4, 17 (16 drafts + 1) and 68 (4 sequences x 17): microseconds per pass and
 effective weight GB/s against the 8 TB/s HBM peak.  ``value`` is the M = 1
 figure of the 449-job step; every batch size is in ``per_m``.
@@ -175,12 +175,16 @@ def time_pass(run, args, probe, wbytes, M, fused, with_unfused):
          "us_p10_p50_p90": percentiles_us(steps_ms),
          "total_algorithmic_gbps": round((wbytes + pass_io_bytes(M, fused)) / (ms * 1e-3) / 1e9, 1),
          "jobs": run.step.info()["jobs"],
-         "schedule": "one persistent launch" if M == 1 else "one launch per job"}
+         "schedule": "one persistent launch" if M == 1 else "one launch per dependency stage"}
     if M != 1:
         e["persistent_us_per_pass"] = round(time_launches(lambda i: run.run_persistent(), args.steps,
                                                           args.warmup) * 1000, 2)
         if run.check():
             raise RuntimeError(f"M={M}: a stage wait timed out in the persistent launch")
+        e["staged_us_per_pass"] = round(time_launches(lambda i: run.run_staged(), args.steps,
+                                                      args.warmup) * 1000, 2)
+        e["per_job_us_per_pass"] = round(time_launches(lambda i: run.run_unfused(), args.steps,
+                                                        args.warmup) * 1000, 2)
     if with_unfused:
         reps = max(2, min(args.steps, 5))
         g = run.capture_unfused()
@@ -528,7 +532,7 @@ def main():
         "config": {"workload": "full synthetic weight pass: 64 layers x {q,k,v,o 5120x5120; gate,up "
                                "17408x5120; down 5120x17408} + lm_head 248320x5120 with argmax/accept "
                                f"(449 NVFP4 matrices as 449 jobs, {PASS_WEIGHT_BYTES} weight bytes), one "
-                               "persistent launch per pass at M=1 (one launch per job at M>=2); the fused "
+                               "persistent launch per pass at M=1 (one launch per stage at M>=2); the fused "
                                "257-job step in per_m[M].fused",
                    "M": ms_list[0], "M_reported": ms_list, "seed": 1004},
         "per_m": per_m,

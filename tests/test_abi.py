@@ -161,6 +161,7 @@ def test_pass_handle_null_checks(lib):
     e = ctypes.c_int()
     assert lib.vg_pass_run(None, None) == VG_ERR_NULL
     assert lib.vg_pass_run_unfused(None, None) == VG_ERR_NULL
+    assert lib.vg_pass_run_staged(None, None) == VG_ERR_NULL
     assert lib.vg_pass_check(None, ctypes.byref(e)) == VG_ERR_NULL
     assert lib.vg_pass_info(None, None, None, None) == VG_ERR_NULL
     assert lib.vg_pass_grid(None, None) == VG_ERR_NULL

@@ -46,14 +46,18 @@ def test_full_step_sampled(weights, M):
         ye, be = oracle.nvfp4_gemm_ref_entries(xs[m["k"]], wq, ws, m["g"], pairs)
         got = np.array([y[a, b] for a, b in pairs], dtype=np.float64)
         assert np.all(np.abs(got - ye) <= be), f"matrix {idx} ({m['name']}, layer {m['layer']})"
-    # the one-launch-per-matrix schedule gives the same bits on every output
+    # the one-launch-per-matrix and one-launch-per-stage schedules give the
+    # same bits on every output
     first = [y.clone() for y in run.y] + [run.argmax.clone(), run.accept_len.clone()]
-    run.run_unfused()
-    torch.cuda.synchronize()
-    again = [y for y in run.y] + [run.argmax, run.accept_len]
-    for a, b in zip(first, again):
-        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
-                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+    for sched in (run.run_unfused, run.run_staged):
+        for y in run.y:
+            y.fill_(float("nan"))
+        sched()
+        torch.cuda.synchronize()
+        again = [y for y in run.y] + [run.argmax, run.accept_len]
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                               b.view(torch.int32) if b.dtype == torch.float32 else b), sched.__name__
     run.close()
 
 
@@ -129,7 +133,7 @@ def test_fused_projections_full_size(weights, M):
     # the schedule vg_pass_run takes for this M (the one the benchmark
     # times), and the other one, give the same bits
     first = [y.clone() for y in fus.y] + [fus.argmax.clone(), fus.accept_len.clone()]
-    for run in (fus.run, fus.run_unfused):
+    for run in (fus.run, fus.run_unfused, fus.run_staged):
         for y in fus.y:
             y.fill_(float("nan"))
         run()

@@ -111,13 +111,19 @@ def test_one_layer_step(M, T):
     p.run_unfused()
     torch.cuda.synchronize()
     assert same(first, snapshot(ys, lm))
+    # so does the one-launch-per-stage schedule (q, k, v in one launch)
+    for y in ys:
+        y.fill_(float("nan"))
+    p.run_staged()
+    torch.cuda.synchronize()
+    assert same(first, snapshot(ys, lm))
     p.close()
 
 
 @pytest.mark.parametrize("M,T", [(1, 1), (4, 1), (17, 17), (68, 17)])
 def test_default_schedule_same_bits(M, T):
     """vg_pass_run takes the persistent launch at M = 1 and one launch per
-    job (narrow matrices sliced) above: the same bits as the persistent
+    stage (narrow matrices sliced) above: the same bits as the persistent
     launch at every M."""
     print(f"[case] default schedule M={M}", flush=True)
     p, host, ys, lm, lmhost = build(M, T, LAYER, (20000, 5120), 36000 + M)
@@ -190,6 +196,13 @@ def test_spread_slices(M):
     p.run_unfused()
     torch.cuda.synchronize()
     assert same(first, snapshot(ys, lm))
+    # one launch per stage: the step's slices, the per-block counts reset
+    for _ in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        p.run_staged()
+        torch.cuda.synchronize()
+        assert same(first, snapshot(ys, lm))
     p.close()
 
 
@@ -206,6 +219,13 @@ def test_odd_shapes_step(M, T):
     check_outputs(M, T, host, ys, lm, lmhost, f"odd M={M}")
     first = snapshot(ys, lm)
     p.run_unfused()
+    torch.cuda.synchronize()
+    assert same(first, snapshot(ys, lm))
+    # one launch per stage: stages of jobs with different K (and K not a
+    # multiple of 128) in one launch
+    for y in ys:
+        y.fill_(float("nan"))
+    p.run_staged()
     torch.cuda.synchronize()
     assert same(first, snapshot(ys, lm))
     p.close()
@@ -228,10 +248,10 @@ def test_step_without_lmhead_and_lmhead_only(M):
 
 
 @pytest.mark.parametrize("M,T,sched", [(1, 1, "run_persistent"), (17, 17, "run_persistent"), (17, 17, "run"),
-                                       (68, 17, "run")])
+                                       (68, 17, "run"), (17, 17, "run_staged")])
 def test_step_graph_replay(M, T, sched):
     """The step (one persistent launch, or the default schedule: one launch
-    per job at M >= 2, narrow matrices sliced) captured in a graph and
+    per stage at M >= 2, narrow matrices sliced) captured in a graph and
     replayed, with eager work and synchronisation between replays: every
     replay equals the eager run."""
     print(f"[case] graph replay M={M} {sched}", flush=True)

@@ -57,6 +57,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "vg_pass_create": (i32, [vp, i32, i32, vp, ctypes.POINTER(vp)]),
         "vg_pass_run": (i32, [vp, vp]),
         "vg_pass_run_unfused": (i32, [vp, vp]),
+        "vg_pass_run_staged": (i32, [vp, vp]),
         "vg_pass_check": (i32, [vp, ctypes.POINTER(i32)]),
         "vg_pass_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "vg_pass_grid": (i32, [vp, ctypes.POINTER(i32)]),
@@ -360,8 +361,9 @@ class LmheadJob(ctypes.Structure):
 class Pass:
     """A whole step (vg_pass_*): GEMM jobs in dependency order plus an
     optional lm_head job.  ``run`` takes the faster schedule for M (one
-    persistent launch at M = 1, one launch per job above),
-    ``run_persistent`` / ``run_unfused`` one of them explicitly.  ``gemms`` is a list
+    persistent launch at M = 1, one launch per stage above),
+    ``run_persistent`` / ``run_staged`` / ``run_unfused`` (one launch per
+    job) one of them explicitly.  ``gemms`` is a list
     of (x, wq, ws, gscale, y, stage[, row_scale]) with torch device tensors
     (row_scale: float32 [N] or None, see vg_gemm_job); ``lmhead`` is
     (x, wq, ws, gscale, T, drafts, argmax, accept_len) or None.  ``parents``,
@@ -423,6 +425,9 @@ class Pass:
 
     def run_unfused(self, stream=None):
         _check(self._lib.vg_pass_run_unfused(self.handle, _stream_ptr(stream)), "vg_pass_run_unfused")
+
+    def run_staged(self, stream=None):
+        _check(self._lib.vg_pass_run_staged(self.handle, _stream_ptr(stream)), "vg_pass_run_staged")
 
     def run_persistent(self, stream=None):
         _check(self._lib.vg_pass_run_persistent(self.handle, _stream_ptr(stream)), "vg_pass_run_persistent")

@@ -71,7 +71,7 @@ struct alignas(128) StageCounter {
 
 struct StreamArgs {
   StreamJob job0;                // the job of a single-job launch (jobs == nullptr)
-  const StreamJob* jobs;         // device array of a step's jobs
+  const StreamJob* jobs;         // device array of a step's jobs (DIRECT: the njobs jobs of one stage)
   const unsigned* stage_total;   // device array: workgroups that signal each stage
   StageCounter (*stage_done)[kDoneSlots];  // [nstages][kDoneSlots]
   StreamCtl* ctl;                // control block (lm_head keys, exit count, error)
@@ -104,7 +104,8 @@ int stream_mt_class(int M, bool invariant);
 int stream_lds_rows(int M, bool invariant);
 // Weight rows per item for a batch of M rows and a reduction length K.
 int stream_rows_per_item(int M, int K, bool invariant, int fmt);
-// DIRECT: grid = items of a.job0.  GRID: a.job0 walked by up to `grid`
+// DIRECT: grid = items of a.job0, or (M >= 2, jobs != nullptr) the items
+// of the njobs jobs at a.jobs, one stage of a step.  GRID: a.job0 walked by up to `grid`
 // resident workgroups.  STATIC: the job list of a step, items assigned
 // round-robin to a grid of co-resident workgroups (at most `grid`).
 hipError_t launch_stream(const StreamArgs& a, int mode, int grid, hipStream_t stream);

@@ -9,10 +9,11 @@
 // by one 256-thread workgroup.  Three launch modes:
 //
 //   * DIRECT: one item per workgroup, dealt by the hardware dispatcher.
-//     A single GEMM, and each job of the step's default M >= 2 schedule
-//     (one launch per job, which measured faster than one persistent launch
-//     there).  With a slice workspace, a narrow matrix's blocks are dealt
-//     as K slices (below) so that every CU has work;
+//     A single GEMM, or the jobs of one stage of a step -- the step's
+//     default M >= 2 schedule (one launch per stage, which measured faster
+//     than one persistent launch there).  With a slice workspace, a narrow
+//     matrix's blocks are dealt as K slices (below) so that every CU has
+//     work;
 //   * GRID: resident workgroups walk the lm_head's blocks;
 //   * STATIC: the whole step as one persistent launch: items numbered in
 //     pass order, dealt round-robin to co-resident workgroups.  An item of
@@ -1220,6 +1221,18 @@ __attribute__((amdgpu_waves_per_eu(MT == 1 && MODE == MODE_DIRECT && FMT == 0 ? 
     auto nodep = [] { return true; };
     const SpreadCtx dsp{a.part, a.part_cnt, &lds_flag};
     NoBest nobest;
+    if constexpr (MT > 0) {
+      if (a.jobs) {
+        // the GEMM jobs of one stage of a step (no dependencies among them)
+        // in one launch: the grid covers their items in list order
+        const int t = a.jobs[0].item_begin + (int)blockIdx.x;
+        int q = 0;
+        while (q + 1 < a.njobs && a.jobs[q + 1].item_begin <= t) ++q;
+        const StreamJob j = a.jobs[q];
+        run_item<MT, FMT, ANYK>(j, t - j.item_begin, a.M, nodep, red, xring, dsp, nobest);
+        return;
+      }
+    }
     run_item<MT, FMT, ANYK>(a.job0, blockIdx.x, a.M, nodep, red, xring, dsp, nobest);
     return;
   } else {

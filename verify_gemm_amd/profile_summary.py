@@ -108,17 +108,17 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
         lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
     lines += ["", "stream_kernel<MT, MODE, FMT, ANYK>: MT 16-row M-tiles (1 at M = 4, 2 at M = 17, 5 at M = 68), "
-              "MODE 0 one GEMM job, 1 the lm_head, 2 the whole pass as one persistent launch; FMT 0 NVFP4; ANYK 0 "
-              "when every K is a multiple of 128.  A launch of step_gemv_kernel (M = 1) or of a MODE 2 kernel is one "
-              "whole pass; vg_pass_run takes the MODE 2 launch at M >= 2 when a stage holds several jobs (the 449-job "
-              f"step) and MODE 0 / 1 launches otherwise (the fused step: {GEMM_JOBS_PER_PASS} GEMM launches and one "
-              "lm_head launch per pass).", ""]
+              "MODE 0 the GEMM jobs of one stage, 1 the lm_head, 2 the whole pass as one persistent launch; FMT 0 "
+              "NVFP4; ANYK 0 when every K is a multiple of 128.  A launch of step_gemv_kernel (M = 1) or of a "
+              "MODE 2 kernel is one whole pass; vg_pass_run takes MODE 0 / 1 launches at M >= 2, one per stage "
+              f"({GEMM_JOBS_PER_PASS} GEMM launches and one lm_head launch per pass, for the 449-job and the "
+              "257-job step alike).", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
 
 
-# The timed step (257 jobs): 64 layers x {q|k|v, o, gate|up, down} GEMMs,
-# then the lm_head.
+# GEMM launches of a pass at M >= 2, one per stage: 64 layers x {q, k, v /
+# q|k|v; o; gate, up / gate|up; down}, then the lm_head.
 GEMM_JOBS_PER_PASS = 256
 
 
@@ -162,19 +162,19 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
               "Traffic per launch (scaled fetch + scaled write) against the pass's algorithmic "
               f"{PASS_WEIGHT_BYTES} weight bytes:", ""]
     # stream_kernel<MT, MODE, FMT, ANYK>: MODE 2 is one persistent launch
-    # of the whole pass; MODE 0 the per-job GEMM launches, MODE 1 the lm_head
+    # of the whole pass; MODE 0 the per-stage GEMM launches, MODE 1 the lm_head
     for k, v in traffic.items():
         a = stream_args(k)
         if k.startswith("step_gemv") or (a is not None and a[1] == 2):
             lines.append(f"* {k} (one launch per pass): {v} bytes ({v / PASS_WEIGHT_BYTES:.3f}x)")
-    # one launch per job: the GEMM launches of a pass (same mix every pass)
+    # one launch per stage: the GEMM launches of a pass (same mix every pass)
     # plus its lm_head launch
     for k, v in traffic.items():
         a = stream_args(k)
         if a is not None and a[1] == 0:
             lm = "stream_kernel<" + ", ".join(str(x) for x in (a[0], 1) + a[2:]) + ">"
             per_pass = v * GEMM_JOBS_PER_PASS + traffic.get(lm, 0)
-            lines.append(f"* {k} x {GEMM_JOBS_PER_PASS} + {lm} (one launch per job): {per_pass} bytes per pass "
+            lines.append(f"* {k} x {GEMM_JOBS_PER_PASS} + {lm} (one launch per stage): {per_pass} bytes per pass "
                          f"({per_pass / PASS_WEIGHT_BYTES:.3f}x)")
     record = {"sources_sha256": sources_hash(), "traffic_bytes": traffic,
               "fetch_scale": f_scale, "write_scale": w_scale}
@@ -210,7 +210,7 @@ def busy(csv_path: str, cmd: str, out: str) -> None:
               f"{SIMDS_PER_SE}); VALU active the same with SQ_ACTIVE_INST_VALU.  This reads the SQ "
               "counters as summed over shader engines (busy cycles) and over SIMDs (MFMA, VALU): a share "
               "of the SIMD cycles while the kernel runs, not an exact utilisation.  MODE 0 kernels are the "
-              "per-job GEMMs of the default schedule, MODE 1 the lm_head, MODE 2 the persistent launch.", ""]
+              "per-stage GEMMs of the default schedule, MODE 1 the lm_head, MODE 2 the persistent launch.", ""]
     with open(out, "w") as f:
         f.write("\n".join(lines))
 

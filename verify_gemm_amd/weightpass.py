@@ -9,8 +9,9 @@ levers"; the veloGB10 docs list a switch to turn the decode graphs off);
 on MI355X the native step executor (vg_pass_run) streams the matrices in
 the per-layer dependency order {q, k, v} -> o -> {gate, up} -> down: at
 M = 1 as ONE persistent launch with device-side stage barriers, at M >= 2
-as one launch per job (the faster schedule there); the other schedule of
-each is kept for comparison (run_persistent / run_unfused).
+as one launch per dependency stage (the faster schedule there); the other
+schedules are kept for comparison (run_persistent / run_staged /
+run_unfused).
 
 This module only holds device buffers and describes the jobs; all
 sequencing and arithmetic happen in libvgemm.so.
@@ -84,7 +85,8 @@ class PassRun:
     top of shared PassWeights, and the step itself as a native vg_pass:
     ``run()`` is the step in vg_pass_run's schedule for this M,
     ``run_persistent()`` one persistent launch of the whole step,
-    ``run_unfused()`` the same work as one launch per job.
+    ``run_unfused()`` the same work as one launch per job,
+    ``run_staged()`` one launch per dependency stage.
 
     ``fused``: {q, k, v} and {gate, up} run as one job each (4 jobs a layer,
     257 in all), reading the members' stacked rows as one matrix; each
@@ -145,6 +147,9 @@ class PassRun:
 
     def run_persistent(self, stream=None):
         self.step.run_persistent(stream)
+
+    def run_staged(self, stream=None):
+        self.step.run_staged(stream)
 
     def capture_unfused(self) -> torch.cuda.CUDAGraph:
         """The one-launch-per-matrix schedule captured into a graph."""
