@@ -15,8 +15,10 @@ HBM before any timed region):
     {gate, up} read as one stacked matrix (257 jobs, each member's tensor
     scale kept as per-row scales, outputs bit-identical to 449 jobs) -- the
     fused projections of dgx-spark-qwen38 README, opening section;
-  * ``per_m[M].roofline``: the pass against the HBM roofline (and at
-    M = 68 the bf16 MFMA roofline too);
+  * ``per_m[M].roofline``: the pass against the HBM roofline (and from
+    M = 17 the bf16 MFMA roofline too), with its HBM traffic per pass from
+    the committed counter summary (the launches that make up a pass in
+    vg_pass_run's schedule);
   * ``configs``: the single matrices of the decode GEMV (M = 1: 17408 x 5120
     and 5120 x 5120) and the verify GEMM (M = 17: 5120 x 17408 and
     17408 x 5120), each timed over >= 1 GiB of distinct rotating weight
@@ -65,15 +67,24 @@ def parse():
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-fused", action="store_true",
                     help="time only the 449-job step (profiles then see one kind of pass launch)")
+    ap.add_argument("--no-alt", action="store_true",
+                    help="at M >= 2 time only vg_pass_run's schedule, not the persistent, per-stage and per-job "
+                         "ones beside it (profiles then see only the default schedule's launches)")
     return ap.parse_args()
 
 
-def step_kernel_name(M: int) -> str:
-    """The kernel one persistent step launch runs: the M = 1 step kernel,
-    else the static-schedule stream kernel <MT, MODE 2, NVFP4, every K a
-    multiple of 128> (every job of the pass has K % 64 == 0 and K <= 18432,
-    so M = 1 always takes the step kernel)."""
-    return "step_gemv_kernel" if M == 1 else f"stream_kernel<{(M + 15) // 16}, 2, 0, 0>"
+def step_kernels(M: int):
+    """The kernels of one pass in vg_pass_run's schedule and how they make
+    it up: at M = 1 one launch of the step kernel; at M >= 2 one launch per
+    dependency stage of the stream kernel <MT, MODE 0, NVFP4, every K a
+    multiple of 128> (256 GEMM stages) and its lm_head launch (MODE 1).
+    Every job of the pass has K % 64 == 0 and K <= 18432, so M = 1 always
+    takes the step kernel."""
+    if M == 1:
+        return {"step_gemv_kernel": 1}, "step_gemv_kernel (the whole 449-job step is one launch of it)"
+    mt = (M + 15) // 16
+    g, lm = f"stream_kernel<{mt}, 0, 0, 0>", f"stream_kernel<{mt}, 1, 0, 0>"
+    return {g: 256, lm: 1}, f"{g} x 256 + {lm} (one launch per dependency stage)"
 
 
 def log(msg):
@@ -136,15 +147,20 @@ def bwprobe(device, gib=8, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when it is missing or the kernel sources changed since."""
+def recorded_traffic(M: int):
+    """HBM bytes of one pass at M in vg_pass_run's schedule from the
+    committed counter summary (per launch, times the launches of a pass),
+    or None when it is missing, lacks one of the kernels or the kernel
+    sources changed since."""
     from verify_gemm_amd import profile_summary
     rec = profile_summary.recorded_traffic(
         os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "step_kernels_full_pass_hbm_traffic.md"))
     if rec is None:
         return None
-    return rec["traffic_bytes"].get(kernel)
+    kernels, _ = step_kernels(M)
+    if any(k not in rec["traffic_bytes"] for k in kernels):
+        return None
+    return int(sum(rec["traffic_bytes"][k] * n for k, n in kernels.items()))
 
 
 def rate_entry(nbytes, ms, probe, extra_bytes=0):
@@ -176,7 +192,7 @@ def time_pass(run, args, probe, wbytes, M, fused, with_unfused):
          "total_algorithmic_gbps": round((wbytes + pass_io_bytes(M, fused)) / (ms * 1e-3) / 1e9, 1),
          "jobs": run.step.info()["jobs"],
          "schedule": "one persistent launch" if M == 1 else "one launch per dependency stage"}
-    if M != 1:
+    if M != 1 and not args.no_alt:
         e["persistent_us_per_pass"] = round(time_launches(lambda i: run.run_persistent(), args.steps,
                                                           args.warmup) * 1000, 2)
         if run.check():
@@ -199,7 +215,8 @@ def pass_roofline(M, us, probe):
     element, 3.41e12 per pass)."""
     achieved = PASS_WEIGHT_BYTES / (us * 1e-6) / 1e9
     r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-         "frac": round(achieved / HBM_PEAK_GBPS, 4), "frac_of_probe": round(achieved / probe, 4)}
+         "frac": round(achieved / HBM_PEAK_GBPS, 4), "frac_of_probe": round(achieved / probe, 4),
+         "traffic": recorded_traffic(M), "kernel": step_kernels(M)[1]}
     if M >= 17:
         tflops = 2.0 * M * PASS_ELEMENTS / (us * 1e-6) / 1e12
         r["mfma"] = {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -519,9 +536,10 @@ def main():
     head = per_m[str(ms_list[0])]
     kus = head["us_per_pass"]
     # the dominant kernel: at M = 1 the step kernel, the whole pass in one
-    # launch; at M >= 2 the persistent launch timed beside the per-job schedule
-    lus = head.get("persistent_us_per_pass", kus)
+    # launch; at M >= 2 the per-stage launches, which together are the pass
+    lus = kus
     achieved = PASS_WEIGHT_BYTES / (lus * 1e-6) / 1e9
+    _, kname = step_kernels(ms_list[0])
     out = {
         "metric": "µs per full weight pass + effective weight GB/s (% HBM peak) at M=1/17/68",
         "value": head["weight_gbps"],
@@ -539,9 +557,8 @@ def main():
         "bwprobe_read_gbps": round(probe, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": recorded_traffic(step_kernel_name(ms_list[0])),
-                     "kernel": (f"{step_kernel_name(ms_list[0])} (the whole 449-job step is one launch of it) "
-                                f"at M={ms_list[0]}"),
+                     "traffic": recorded_traffic(ms_list[0]),
+                     "kernel": f"{kname} at M={ms_list[0]}",
                      "avg_us": lus, "bytes_per_launch": PASS_WEIGHT_BYTES},
     }
     if args.config == "all":
