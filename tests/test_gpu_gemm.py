@@ -129,6 +129,28 @@ def test_bitwise_repeatable(m, n, k):
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("m,k", [(1, 5120), (1, 17408), (1, 2048), (17, 5120)])
+def test_row_bits_independent_of_matrix_height(m, k):
+    """A row's output bits do not depend on how many other rows the launch
+    has: the first rows of a 5120-row matrix, launched alone as matrices of
+    256, 300 and 1000 rows, give the same bits.  At M = 1 the row split
+    then gives a workgroup 1-4 rows of a chunk instead of 20, so its waves
+    lay out one row per half-wave instead of two (the summation must not
+    change with the layout)."""
+    print(f"[case] row bits vs matrix height M={m} K={k}", flush=True)
+    rng = np.random.default_rng(9600 + m + k)
+    wq, ws = synth.gen_weights(rng, 5120, k)
+    x = synth.gen_x(rng, m, k)
+    xd = dev_bf16(x)
+    big = binding.nvfp4_gemm(xd, dev_u8(wq), dev_u8(ws), 1.25).cpu().numpy()
+    for n in (256, 300, 1000):
+        small = binding.nvfp4_gemm(xd, dev_u8(wq[:n].copy()), dev_u8(ws[:n].copy()), 1.25).cpu().numpy()
+        assert np.array_equal(small.view(np.uint32), big[:, :n].view(np.uint32)), f"N={n}"
+    y_ref, bound = oracle.nvfp4_gemm_ref(x, wq[:300], ws[:300], 1.25)
+    ok, worst, at = within_bound(big[:, :300], y_ref, bound)
+    assert ok, f"worst err/bound {worst:.3g} at {at}"
+
+
 @pytest.mark.parametrize("m,n,k", [(2, 5120, 17408), (17, 333, 5120), (68, 1000, 2048), (17, 5120, 5120)])
 def test_sliced_gemm_same_bits(m, n, k):
     """With a workspace, nvfp4_gemm_ex deals a narrow matrix's K slices to

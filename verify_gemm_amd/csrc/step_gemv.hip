@@ -218,8 +218,11 @@ __device__ __forceinline__ void wave_rows(int rows, int w, int& begin, int& coun
 // half-wave, not the 3 that K = 5120 allows (measured: those chunks
 // computed 6 rows per wave for 3 or 4 real ones).
 __device__ __forceinline__ int wave_rh(int k, int count) {
-  const int r = (count + 1) >> 1, m = rows_per_half(k);
-  return r < m ? (r > 0 ? r : 1) : m;
+  // never below two when K allows two: the one-row layout sums a row in
+  // another order (four chains per piece), so it is kept for the K that
+  // allow only one row per half-wave, and a row's bits depend on K alone
+  const int r = (count + 1) >> 1, m = rows_per_half(k), lo = m < 2 ? m : 2;
+  return r < lo ? lo : (r < m ? r : m);
 }
 
 // Walks this workgroup's chunks in job order (the same in every wave).
@@ -320,11 +323,15 @@ __device__ __forceinline__ void issue(const StreamJob& j, const Chunk& ch, int w
 // a dependent dot2 comes several instructions after the previous one on
 // its chain and the decode and dot2 latencies hide inside one wave; a
 // chain-at-a-time order runs at about a third of the issue rate.
-//   * BLK (two or three rows per half-wave): one eight-deep chain per
-//     16-element block, 2*G chains, started from zero once per block and
-//     applied with one FMA -- the fewest instructions per code;
-//   * otherwise (one row): 4*G four-deep chains, one per code word, two
-//     added per block, so that even one slot keeps four chains in flight.
+//   * BLK (two or three rows per half-wave: every K <= 9216, whatever a
+//     wave's own row count): one eight-deep chain per 16-element block,
+//     2*G chains, started from zero once per block and applied with one
+//     FMA -- the fewest instructions per code;
+//   * otherwise (one row per half-wave: K > 9216): 4*G four-deep chains,
+//     one per code word, two added per block, so that even one slot keeps
+//     four chains in flight.
+// The form depends on K alone, so a row's sum does not depend on the
+// chunk or wave it lands in.
 template <int G, int S0, int SS, int NX, bool BLK>
 __device__ __forceinline__ void piece_group(const Buf& b, const u32x4 (&x)[NX][4], const f32x2 (&s)[G],
                                             float (&acc)[G]) {
