@@ -231,6 +231,32 @@ def test_odd_shapes_step(M, T):
     p.close()
 
 
+WIDE = [(640, 1024, 0), (64, 1024, 0), (1000, 1024, 0), (1, 1024, 0), (300, 1024, 0), (128, 2048, 1),
+        (2049, 1024, 2)]
+
+
+@pytest.mark.parametrize("M", [2, 17, 33])
+def test_many_jobs_in_one_stage(M):
+    """A stage of five matrices of different heights (one of a single row):
+    the per-stage schedule launches them together, their blocks in list
+    order; the bits equal the persistent launch's and the per-job
+    schedule's, and every output is within the oracle's bound."""
+    print(f"[case] five-job stage M={M}", flush=True)
+    p, host, ys, lm, lmhost = build(M, 1, WIDE, (700, 1024), 37000 + M)
+    p.run_persistent()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    check_outputs(M, 1, host, ys, lm, lmhost, f"five-job stage M={M}")
+    first = snapshot(ys, lm)
+    for sched in (p.run_staged, p.run_unfused, p.run):
+        for y in ys:
+            y.fill_(float("nan"))
+        sched()
+        torch.cuda.synchronize()
+        assert same(first, snapshot(ys, lm)), sched.__name__
+    p.close()
+
+
 @pytest.mark.parametrize("M", [1, 17])
 def test_step_without_lmhead_and_lmhead_only(M):
     p, host, ys, lm, lmhost = build(M, 1, LAYER[:4], None, 33000 + M)
