@@ -93,25 +93,32 @@ def log(msg):
 
 def time_launches(fn, steps, warmup, per_step=None):
     """Average ms of `fn` (work enqueued on the current stream), timed with
-    events recorded on that stream.  With a list `per_step`, an event
-    between consecutive steps also gives each step's ms (appended to it).
-    `fn` takes the step index."""
+    two events recorded on that stream around `steps` calls.  With a list
+    `per_step`, a second run of `steps` calls with an event between
+    consecutive calls gives each call's ms (appended to it); those events
+    sit between the launches, so they are kept out of the average (they add
+    a few µs per call, which matters for a call of 10-20 µs).  `fn` takes
+    the step index."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step is not None else 2)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(s)
     for i in range(steps):
         fn(i)
-        if per_step is not None:
-            ev[i + 1].record(s)
-    ev[-1].record(s)
+    ev[1].record(s)
     torch.cuda.synchronize()
     if per_step is not None:
-        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    return ev[0].elapsed_time(ev[-1]) / steps
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(s)
+        for i in range(steps):
+            fn(i)
+            evs[i + 1].record(s)
+        torch.cuda.synchronize()
+        per_step.extend(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[1]) / steps
 
 
 def percentiles_us(ms_list):
