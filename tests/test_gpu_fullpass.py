@@ -95,8 +95,8 @@ def _bits(t):
 def test_fused_projections_full_size(weights, M):
     """{q, k, v} and {gate, up} as one job each (257 jobs, each member's
     tensor scale kept as per-row scales): the same bits as the separate
-    jobs, in the one-launch and the one-launch-per-job schedules; sampled
-    fused outputs against the oracle."""
+    jobs, in vg_pass_run's schedule, one launch per job and one launch per
+    stage; sampled fused outputs against the oracle."""
     print(f"[case] fused projections M={M}", flush=True)
     sep = weightpass.PassRun(weights, M)
     fus = weightpass.PassRun(weights, M, fused=True)

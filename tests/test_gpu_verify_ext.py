@@ -210,8 +210,9 @@ def test_pass_batch_invariant_rows_and_tree():
 @pytest.mark.parametrize("M", [1, 4, 17, 33, 52, 68])
 def test_row_scales_stack_matrices_bitwise(M):
     """Two matrices stacked by rows as one job with per-row scales (each
-    member's own tensor scale) give the same bits as two jobs, in the
-    one-launch and one-launch-per-job schedules, and lie within the
+    member's own tensor scale) give the same bits as two jobs, in every
+    schedule (one persistent launch, one launch per stage, one launch per
+    job, and vg_pass_run's choice), and lie within the
     oracle's bound with each member's own g.  K = 5120 and 17408 (the step
     kernel at M = 1; the LDS-shared MFMA item with one to five M-tiles
     above, the five-tile compact ring at M = 68, K slices dealt as separate
@@ -233,7 +234,7 @@ def test_row_scales_stack_matrices_bitwise(M):
         yf = torch.empty((M, 512), device="cuda")
         sep = binding.Pass([(x, wq[:304], ws[:304], gs[0], ya, 0), (x, wq[304:], ws[304:], gs[1], yb, 0)], M)
         fus = binding.Pass([(x, wq, ws, 123.0, yf, 0, rs)], M)   # gscale ignored with row scales
-        for run in ("run", "run_persistent", "run_unfused"):
+        for run in ("run", "run_persistent", "run_staged", "run_unfused"):
             yf.fill_(float("nan"))
             getattr(sep, run)()
             getattr(fus, run)()
