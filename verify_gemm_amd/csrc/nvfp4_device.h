@@ -73,11 +73,12 @@ __device__ __forceinline__ f32x2 e2m1x2_f32(unsigned w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, sel);
 }
 
+// Two fp32 values that bf16 holds exactly (a = s * e has at most 6
+// significant bits, so the low 16 bits of its fp32 form are zero) as a
+// bf16 pair: their high halves, gathered by one byte permute (v_perm_b32
+// runs at twice the rate of the fp32-to-bf16 conversion).
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  bf16x2 v;
-  v[0] = (__bf16)a;  // exact: a = s * e has at most 6 significant bits
-  v[1] = (__bf16)b;
-  return __builtin_bit_cast(unsigned, v);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(unsigned, b), __builtin_bit_cast(unsigned, a), 0x07060302u);
 }
 
 // One code dword (8 elements of one 16-block) times its block scale s, as

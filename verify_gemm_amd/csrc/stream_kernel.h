@@ -464,13 +464,19 @@ struct MfmaLdsItem {
     }
   }
 
-  __device__ __forceinline__ void store_x(int p, unsigned char* slot) {
+  // With the compact ring (slots M rows apart) a row m >= M of slot 0
+  // would land on slot 1's rows: it goes to row M + m of the ring instead,
+  // the tail past slot 1's rows, which only MFMA rows past M read.  (Slot
+  // 1's own rows m >= M are that tail already.)  An address select, not a
+  // branch: the rows of one write differ between the half-waves.
+  __device__ __forceinline__ void store_x(int p, unsigned char* slot, unsigned char* ring) {
     const unsigned piece = threadIdx.x & 31;
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
       const int m = xrow(i);
-      if (!kCompact || m < mrows)
-        *reinterpret_cast<u32x4*>(slot + 512 * m + 16 * (piece ^ (unsigned)(m & 15))) = xq[p][i];
+      unsigned char* row = slot + 512 * m;
+      if constexpr (kCompact) row = m < mrows ? row : ring + 512 * (mrows + m);
+      *reinterpret_cast<u32x4*>(row + 16 * (piece ^ (unsigned)(m & 15))) = xq[p][i];
     }
   }
 
@@ -520,7 +526,13 @@ struct MfmaLdsItem {
     read(0, a[0]);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
+      // With three or more M-tiles the compiler otherwise sinks each read
+      // next to its MFMA and waits for it there (measured: M = 68 2.8 %
+      // faster pinned; with one or two M-tiles pinning costs registers and
+      // is slower).
+      if constexpr (MT >= 3) __builtin_amdgcn_sched_barrier(0);
       if (st + 1 < 8) read(st + 1, a[(st + 1) & 1]);
+      if constexpr (MT >= 3) __builtin_amdgcn_sched_barrier(0);
       bf16x8 b[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -553,7 +565,7 @@ struct MfmaLdsItem {
         acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         tot[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    store_x(0, lds);
+    store_x(0, lds, lds);
     // The loop over whole groups of P windows must be entered in the order
     // its own iterations leave the loads in, and contain no skipped load:
     // a loop header reached with another order (the first P windows' loads
@@ -604,7 +616,7 @@ struct MfmaLdsItem {
       window(p, lds + (i & 1) * slot_bytes);
       if (v0 + i + 1 == fold_at) fold();
     }
-    store_x(p + 1 < P ? p + 1 : 0, lds + ((i + 1) & 1) * slot_bytes);
+    store_x(p + 1 < P ? p + 1 : 0, lds + ((i + 1) & 1) * slot_bytes, lds);
     load_x(p, v0 + i + P);
     load_w(p, v0 + i + P);
   }
