@@ -77,13 +77,16 @@ def step_kernels(M: int):
     """The kernels of one pass in vg_pass_run's schedule and how they make
     it up: at M = 1 one launch of the step kernel; at M >= 2 one launch per
     dependency stage of the stream kernel <MT, MODE 0, NVFP4, every K a
-    multiple of 128> (256 GEMM stages) and its lm_head launch (MODE 1).
+    multiple of 128, XH> (256 GEMM stages) and its lm_head launch (MODE 1);
+    XH = 1 when the last M-tile is at most half used (M <= 16 MT - 8, MT <= 4;
+    the one-tile lm_head keeps XH = 0).
     Every job of the pass has K % 64 == 0 and K <= 18432, so M = 1 always
     takes the step kernel."""
     if M == 1:
         return {"step_gemv_kernel": 1}, "step_gemv_kernel (the whole 449-job step is one launch of it)"
     mt = (M + 15) // 16
-    g, lm = f"stream_kernel<{mt}, 0, 0, 0>", f"stream_kernel<{mt}, 1, 0, 0>"
+    xh = 1 if mt <= 4 and M <= 16 * mt - 8 else 0
+    g, lm = f"stream_kernel<{mt}, 0, 0, 0, {xh}>", f"stream_kernel<{mt}, 1, 0, 0, {xh if mt >= 2 else 0}>"
     return {g: 256, lm: 1}, f"{g} x 256 + {lm} (one launch per dependency stage)"
 
 

@@ -107,9 +107,10 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
             continue
         lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    lines += ["", "stream_kernel<MT, MODE, FMT, ANYK>: MT 16-row M-tiles (1 at M = 4, 2 at M = 17, 5 at M = 68), "
+    lines += ["", "stream_kernel<MT, MODE, FMT, ANYK, XH>: MT 16-row M-tiles (1 at M = 4, 2 at M = 17, 5 at M = 68), "
               "MODE 0 the GEMM jobs of one stage, 1 the lm_head, 2 the whole pass as one persistent launch; FMT 0 "
-              "NVFP4; ANYK 0 when every K is a multiple of 128.  A launch of step_gemv_kernel (M = 1) or of a "
+              "NVFP4; ANYK 0 when every K is a multiple of 128; XH 1 when the last M-tile is at most half used "
+              "(M <= 16 MT - 8: eight activation rows fewer per window).  A launch of step_gemv_kernel (M = 1) or of a "
               "MODE 2 kernel is one whole pass; vg_pass_run takes MODE 0 / 1 launches at M >= 2, one per stage "
               f"({GEMM_JOBS_PER_PASS} GEMM launches and one lm_head launch per pass, for the 449-job and the "
               "257-job step alike).", ""]
@@ -161,7 +162,7 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
               "smaller fills of the same run are left out).", "",
               "Traffic per launch (scaled fetch + scaled write) against the pass's algorithmic "
               f"{PASS_WEIGHT_BYTES} weight bytes:", ""]
-    # stream_kernel<MT, MODE, FMT, ANYK>: MODE 2 is one persistent launch
+    # stream_kernel<MT, MODE, FMT, ANYK, XH>: MODE 2 is one persistent launch
     # of the whole pass; MODE 0 the per-stage GEMM launches, MODE 1 the lm_head
     for k, v in traffic.items():
         a = stream_args(k)
