@@ -110,7 +110,8 @@ def trace(stats_csv: str, cmd: str, out: str) -> None:
     lines += ["", "stream_kernel<MT, MODE, FMT, ANYK, XH>: MT 16-row M-tiles (1 at M = 4, 2 at M = 17, 5 at M = 68), "
               "MODE 0 the GEMM jobs of one stage, 1 the lm_head, 2 the whole pass as one persistent launch; FMT 0 "
               "NVFP4; ANYK 0 when every K is a multiple of 128; XH 1 when the last M-tile is at most half used "
-              "(M <= 16 MT - 8: eight activation rows fewer per window).  A launch of step_gemv_kernel (M = 1) or of a "
+              "(M <= 16 MT - 8: eight activation rows fewer per window; the one-tile lm_head keeps XH 0).  A launch of "
+              "step_gemv_kernel (M = 1) or of a "
               "MODE 2 kernel is one whole pass; vg_pass_run takes MODE 0 / 1 launches at M >= 2, one per stage "
               f"({GEMM_JOBS_PER_PASS} GEMM launches and one lm_head launch per pass, for the 449-job and the "
               "257-job step alike).", ""]
@@ -173,7 +174,9 @@ def pmc(fetch_csv: str, write_csv: str, cmd_f: str, cmd_w: str, probe_bytes: int
     for k, v in traffic.items():
         a = stream_args(k)
         if a is not None and a[1] == 0:
-            lm = "stream_kernel<" + ", ".join(str(x) for x in (a[0], 1) + a[2:]) + ">"
+            # the one-tile lm_head keeps the full activation loads (XH 0)
+            lm_args = (a[0], 1) + a[2:4] + ((a[4] if a[0] >= 2 else 0),) + a[5:] if len(a) > 4 else (a[0], 1) + a[2:]
+            lm = "stream_kernel<" + ", ".join(str(x) for x in lm_args) + ">"
             per_pass = v * GEMM_JOBS_PER_PASS + traffic.get(lm, 0)
             lines.append(f"* {k} x {GEMM_JOBS_PER_PASS} + {lm} (one launch per stage): {per_pass} bytes per pass "
                          f"({per_pass / PASS_WEIGHT_BYTES:.3f}x)")
