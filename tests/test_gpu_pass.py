@@ -235,12 +235,13 @@ WIDE = [(640, 1024, 0), (64, 1024, 0), (1000, 1024, 0), (1, 1024, 0), (300, 1024
         (2049, 1024, 2)]
 
 
-@pytest.mark.parametrize("M", [2, 17, 33])
+@pytest.mark.parametrize("M", [1, 2, 17, 33])
 def test_many_jobs_in_one_stage(M):
     """A stage of five matrices of different heights (one of a single row):
-    the per-stage schedule launches them together, their blocks in list
-    order; the bits equal the persistent launch's and the per-job
-    schedule's, and every output is within the oracle's bound."""
+    at M >= 2 the per-stage schedule launches them together, their blocks in
+    list order; at M = 1 the step kernel gives each matrix its own run of
+    workgroups (the one-row matrix a single workgroup).  The bits equal the
+    other schedules', and every output is within the oracle's bound."""
     print(f"[case] five-job stage M={M}", flush=True)
     p, host, ys, lm, lmhost = build(M, 1, WIDE, (700, 1024), 37000 + M)
     p.run_persistent()

@@ -13,11 +13,13 @@ constexpr int VG_MAX_M_DEV = 68;
 constexpr int kKeySlots = 16;     // atomic-max slots per lm_head row
 constexpr int kMaxStages = 1024;  // dependency stages of one step
 
-// One NVFP4 matrix of a step.  Items are contiguous blocks of
-// rows_per_item weight rows (all of K) -- or, from a spread job's first
-// spread block f on, one K slice of such a block (item f + (b - f) * S + s
-// is slice s of block b, S = lds_slices(k)); jobs are listed in pass order
-// and their items are numbered consecutively from item_begin.
+// One NVFP4 matrix of a step.  For the stream kernels, items are
+// contiguous blocks of rows_per_item weight rows (all of K) -- or, from a
+// spread job's first spread block f on, one K slice of such a block (item
+// f + (b - f) * S + s is slice s of block b, S = lds_slices(k)); jobs are
+// listed in pass order and their items are numbered consecutively from
+// item_begin.  The M = 1 step kernel has no items: the same four words hold
+// the job's rows per workgroup (step_rows).
 struct StreamJob {
   const uint8_t* wq;  // [n][k/2]
   const uint8_t* ws;  // [n][k/16]
@@ -28,14 +30,47 @@ struct StreamJob {
   int n;
   int k;
   int stage;          // dependency stage (non-decreasing along the list)
-  int item_begin;
-  int items;
   int kind;           // 0: GEMM, 1: lm_head (argmax, no output matrix)
   int fmt;            // weight format: 0 NVFP4 (wq codes, ws block scales), 1 FP8 E4M3 (wq [n][k] bytes)
-  int spread;         // 0, or 1 + the first block whose K slices are separate items (a step, M >= 2)
-  int part_base;      // spread: partial slot of the job's first slice item (StreamArgs::part / part_cnt)
+  union {
+    struct {            // stream kernels
+      int item_begin;
+      int items;
+      int spread;       // 0, or 1 + the first block whose K slices are separate items (a step, M >= 2)
+      int part_base;    // spread: partial slot of the job's first slice item (StreamArgs::part / part_cnt)
+    };
+    struct {            // step kernel: the rows go to wgn workgroups from wg0 on (cyclically);
+      int wg0;          // the i-th of them takes rq rows, one more if i < rr, in order
+      int wgn;
+      int rq;
+      int rr;
+    };
+  };
 };
 static_assert(sizeof(StreamJob) % 16 == 0, "the job table is copied in 16-byte pieces");
+
+// The step kernel's rows of job j in workgroup w of a grid of G: returns
+// the count and sets pos to the first row (0 rows: w is not one of the
+// job's workgroups).  Host and kernel use this one rule.
+__host__ __device__ __forceinline__ int step_rows(const StreamJob& j, int w, int G, int& pos) {
+  int i = w - j.wg0;
+  if (i < 0) i += G;
+  if (i >= j.wgn) {
+    pos = 0;
+    return 0;
+  }
+  pos = i * j.rq + (i < j.rr ? i : j.rr);
+  return j.rq + (i < j.rr ? 1 : 0);
+}
+
+// Splits job j's rows as equally as rows allow over wgn workgroups from
+// wg0 on (wg0 < G, wgn <= G).
+inline void set_step_rows(StreamJob& j, int wg0, int wgn) {
+  j.wg0 = wg0;
+  j.wgn = wgn;
+  j.rq = j.n / wgn;
+  j.rr = j.n % wgn;
+}
 
 // K slices of the M >= 2 MFMA item (K % 128 == 0): a block's sum over K is
 // taken slice by slice, each slice summed from zero over its 256-element
@@ -118,7 +153,9 @@ int stream_max_grid();
 int stream_num_cus();
 
 // M = 1: the whole step (or a single GEMM / lm_head) as one launch of
-// step_gemv_grid() resident workgroups; rows of every job split evenly.
+// step_gemv_grid() resident workgroups.  A multi-job launch (a.jobs) takes
+// each job's rows per workgroup from its step fields (set_step_rows); a
+// single job (a.job0) is split evenly over the grid here.
 // Every job's K must satisfy step_gemv_supports (K % 64 == 0, K <= 18432);
 // other M = 1 shapes take the stream kernel.
 // A step launch holds at most kStepMaxJobs jobs (its job table lives in LDS).

@@ -47,11 +47,15 @@
 // The job table is copied into LDS at the start, so reading a job
 // descriptor never waits on memory.
 //
-// Work split: every matrix's rows are divided EVENLY over the G workgroups
-// (workgroup w owns rows [N*w/G, N*(w+1)/G) of every matrix), so each
-// dependency stage ({q,k,v} -> o -> {gate,up} -> down per layer, then the
-// lm_head) is balanced to a row; a workgroup's rows of one matrix are cut
-// into equal chunks of at most 8 * (18 / ceil(K/1024)) rows.
+// Work split: each dependency stage ({q,k,v} -> o -> {gate,up} -> down per
+// layer, then the lm_head) is balanced to a row over the G workgroups.  A
+// stage of one matrix splits its rows evenly over all of them; the host may
+// instead give the matrices of a stage disjoint runs of workgroups in
+// proportion to their bytes (q, k, v of 5120 rows: 85, 85 and 86 of 256
+// workgroups, 60 or 61 rows each, rather than 20 rows of each matrix on
+// every workgroup), which keeps a workgroup's rows in one matrix and its
+// chunks large.  A workgroup's rows of one matrix are cut into equal
+// chunks of at most 12 * rows_per_half(K) rows (36 at K = 5120).
 //
 // Arithmetic: half-wave h of a compute wave owns rows 2i + h of the wave's
 // rows; lane L reads 16-byte code pieces L, L+32, ... of the row (512
@@ -228,7 +232,7 @@ __device__ __forceinline__ int wave_rh(int k, int count) {
 // Walks this workgroup's chunks in job order (the same in every wave).
 // The chunk walk runs in every wave between chunks, so it avoids runtime
 // divisions (software sequences on this GPU): the workgroup's rows come
-// from a shift when the grid is a power of two, a job's chunk count from a
+// from the job's precomputed split (step_rows), a job's chunk count from a
 // constant divisor, and the chunk sizes from one quotient and remainder
 // per job.
 struct Cursor {
@@ -236,28 +240,12 @@ struct Cursor {
   int idx = 0, base = 0, rem = 0;  // chunk ordinal in the job; the first rem chunks have base + 1 rows, the rest base
 };
 
-// Rows [pos, end) of a job with n rows belong to this workgroup: an even
-// split over the grid, floor(n * w / G) .. floor(n * (w + 1) / G).
-__device__ __forceinline__ void job_rows(int n, int& pos, int& end) {
-  const unsigned G = gridDim.x, w = blockIdx.x;
-  if ((G & (G - 1)) == 0 && G <= 1024 && n <= (1 << 21)) {  // n * G < 2^32
-    const int s = __builtin_ctz(G);
-    pos = (int)(((unsigned)n * w) >> s);
-    end = (int)(((unsigned)n * (w + 1)) >> s);
-  } else {
-    pos = (int)((long long)n * w / G);
-    end = (int)((long long)n * (w + 1) / G);
-  }
-}
-
 __device__ __forceinline__ bool next_chunk(const Shared& sh, int njobs, Cursor& cu, Chunk& out) {
   static_assert(2 * kCW == 12, "chunk caps below are 12 * rows_per_half");
   while (cu.left == 0) {
     if (cu.job >= njobs) return false;
     const StreamJob j = lds_job(sh, cu.job);
-    int end;
-    job_rows(j.n, cu.pos, end);
-    const int rows = end - cu.pos;
+    const int rows = step_rows(j, (int)blockIdx.x, (int)gridDim.x, cu.pos);
     // chunks of at most chunk_cap(k) rows, as equal as rows allow: the
     // first rows % cnt of them one row larger
     const int rh = rows_per_half(j.k);
@@ -907,7 +895,10 @@ bool step_gemv_supports(int K) { return K >= 64 && K % 64 == 0 && K <= kMaxK; }
 int step_gemv_grid() { return num_cus(); }
 
 hipError_t launch_step_gemv(const StreamArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(step_gemv_kernel, dim3(step_gemv_grid()), dim3(kWG), 0, stream, a);
+  const int G = step_gemv_grid();
+  StreamArgs b = a;
+  if (!b.jobs) set_step_rows(b.job0, 0, G);
+  hipLaunchKernelGGL(step_gemv_kernel, dim3(G), dim3(kWG), 0, stream, b);
   return hipGetLastError();
 }
 
