@@ -4,7 +4,9 @@
 compiles every HIP source under ``csrc/`` into ``verify_gemm_amd/libvgemm.so``:
 each source to an object file (in parallel: the stream kernel's variants
 sit in one translation unit per M-tile class and weight format), then one
-link.
+link.  It also links ``libvgemm_stamps.so``, the same library with the M = 1
+step kernel built with VG_STAGE_STAMPS (per-stage timestamps, read by
+``verify_gemm_amd.stage_stamps``); nothing else loads it.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvgemm.so")
+LIB_STAMPS = os.path.join(PKG, "libvgemm_stamps.so")
 SOURCES = (["api.cpp", "stream.hip", "step_gemv.hip", "bwprobe.hip", "noalloc.hip"]
            + [f"stream_mt{mt}_f{fmt}.hip" for mt in range(6) for fmt in range(2)])
 ARCH = "gfx950"
@@ -50,9 +53,10 @@ def build(verbose: bool = False) -> str:
     """Compile libvgemm.so (always rebuilds).  Returns its path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="vgemm_build_") as tmp:
-        def compile_one(src):
-            obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        def compile_one(task):
+            src, defs = task
+            obj = os.path.join(tmp, src + ("".join(defs) if defs else "") + ".o")
+            cmd = [cc, *HIPCC_FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             res = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,21 +64,25 @@ def build(verbose: bool = False) -> str:
 
         # the slowest translation units first
         order = sorted(SOURCES, key=lambda f: (not f.startswith("stream_mt"), f))
+        tasks = [(src, []) for src in order] + [("step_gemv.hip", ["-DVG_STAGE_STAMPS"])]
         with concurrent.futures.ThreadPoolExecutor(_jobs()) as ex:
-            results = list(ex.map(compile_one, order))
+            results = list(ex.map(compile_one, tasks))
         for src, _, res in results:
             if res.returncode != 0:
                 sys.stderr.write(res.stdout + res.stderr)
                 raise RuntimeError(f"hipcc failed on {src} with exit code {res.returncode}")
-        out_tmp = LIB + ".tmp"
-        cmd = [cc, f"--offload-arch={ARCH}", "-fPIC", "-shared", *[obj for _, obj, _ in results], "-o", out_tmp]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
-    os.replace(out_tmp, LIB)
+        plain = [obj for _, obj, _ in results[:len(order)]]
+        stamped = [results[-1][1] if src == "step_gemv.hip" else obj for (src, obj, _) in results[:len(order)]]
+        for lib, objs in ((LIB, plain), (LIB_STAMPS, stamped)):
+            cmd = [cc, f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", lib + ".tmp"]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError(f"hipcc link of {os.path.basename(lib)} failed with exit code {res.returncode}")
+    os.replace(LIB_STAMPS + ".tmp", LIB_STAMPS)
+    os.replace(LIB + ".tmp", LIB)
     return LIB
 
 

@@ -90,6 +90,28 @@ namespace vg {
 
 namespace {
 
+// Stage timestamps, compiled in only for the diagnostic library
+// (libvgemm_stamps.so, built beside libvgemm.so with VG_STAGE_STAMPS): per
+// stage s and workgroup, the s_memrealtime (100 MHz) time at which
+//   kStampDetect  the I/O wave saw stage s - 1 complete,
+//   kStampReady   stage s's first activation row and scales were in LDS,
+//   kStampDone    the compute waves had finished the stage's last chunk,
+//   kStampSignal  its result stores had completed, just before the signal.
+// Each stamp is one extra global store of lane 0 of the wave that takes it,
+// so the timed pass runs slightly slower than the product build.
+#ifdef VG_STAGE_STAMPS
+constexpr int kStampStages = 1024, kStampWGs = 256;
+enum { kStampDetect, kStampReady, kStampDone, kStampSignal, kStampKinds };
+__device__ unsigned long long g_stamps[kStampKinds][kStampStages][kStampWGs];
+__device__ __forceinline__ void stamp(int kind, int s) {
+  if ((threadIdx.x & 63) == 0 && s >= 0 && s < kStampStages && blockIdx.x < (unsigned)kStampWGs)
+    g_stamps[kind][s][blockIdx.x] = __builtin_amdgcn_s_memrealtime();
+}
+#else
+enum { kStampDetect, kStampReady, kStampDone, kStampSignal };
+__device__ __forceinline__ void stamp(int, int) {}
+#endif
+
 constexpr int kCW = 6;                  // compute waves
 constexpr int kIO = kCW;                // index of the I/O wave
 constexpr int kST = kCW + 1;            // index of the store wave
@@ -654,6 +676,7 @@ __device__ void stage_scales(const StreamJob& j, const Chunk& ch, Shared& sh, in
 
 __device__ void signal_stage(const StreamArgs& a, int s) {
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's result stores have completed
+  stamp(kStampSignal, s);
   if ((threadIdx.x & 63) == 0)
     __hip_atomic_fetch_add(&a.stage_done[s][blockIdx.x % kDoneSlots].v, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -671,11 +694,14 @@ struct IoState {
 // Loads complete in order, so "at most kScaleDma outstanding" means every
 // load issued before that DMA -- this chunk's scales included -- is done.
 __device__ void prepare(const StreamArgs& a, Shared& sh, const StreamJob& j, IoState& st, bool ahead) {
+  bool waited = false;
   if (j.stage != st.ep.stage && a.waits) {
     const int need = j.stage - 1;
     if (need >= 0 && need > st.done_stage) {
       (void)wait_stage(a, need, a.stage_total[need]);  // a time-out raises the error flag
       st.done_stage = need;
+      waited = true;
+      stamp(kStampDetect, j.stage);
     }
   }
   if (st.ep.advance(j)) stage_x(j, sh.xs[st.ep.n & 1]);
@@ -683,6 +709,7 @@ __device__ void prepare(const StreamArgs& a, Shared& sh, const StreamJob& j, IoS
     __builtin_amdgcn_s_waitcnt(kWaitVmScale);
   else
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (waited) stamp(kStampReady, j.stage);
 }
 
 // Stores the results of chunk ch (LDS area `parity`; lane t owns row t)
@@ -776,6 +803,7 @@ __device__ __forceinline__ void store_loop(const StreamArgs& a, Shared& sh, int 
     const int lane = threadIdx.x & 63;
     const float rsc = j.kind == 0 && j.gr && lane < cur.rows ? j.gr[cur.r0 + lane] : 1.0f;
     wait_done(a, sh, parity);
+    if (!more || lds_job(sh, nxt.job).stage != j.stage) stamp(kStampDone, j.stage);
     flush(sh, j, cur, parity, rsc);
     // the LDS reads of the flush have completed before the areas are handed back
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -902,3 +930,12 @@ hipError_t launch_step_gemv(const StreamArgs& a, hipStream_t stream) {
 }
 
 }  // namespace vg
+
+#ifdef VG_STAGE_STAMPS
+// Diagnostic library only: copies the stamps of the last step launch into
+// out[kind][stage][workgroup] (4 x 1024 x 256 values; slots a launch did
+// not stamp keep older values).  Returns 0, or 1 on a HIP error.
+extern "C" int vg_stage_stamps(unsigned long long* out) {
+  return hipMemcpyFromSymbol(out, HIP_SYMBOL(vg::g_stamps), sizeof(vg::g_stamps)) == hipSuccess ? 0 : 1;
+}
+#endif
