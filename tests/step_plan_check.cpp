@@ -91,6 +91,19 @@ int main() {
   jobs.push_back(lm);
   if (!check(jobs, 256, 5)) return 1;
   for (const StreamJob& j : jobs) printf("layer job n=%d k=%d stage=%d wg0=%d wgn=%d\n", j.n, j.k, j.stage, j.wg0, j.wgn);
+  // a stage that keeps the even split on 256 workgroups (a partition's
+  // largest share would be above 33/32 of it), its extra rows rotated
+  std::vector<StreamJob> spread;
+  const int sn[3] = {491, 768, 300}, sk[3] = {1024, 1024, 64};
+  for (int i = 0; i < 3; ++i) {
+    StreamJob j{};
+    j.n = sn[i];
+    j.k = sk[i];
+    j.stage = 0;
+    spread.push_back(j);
+  }
+  if (!check(spread, 256, 1)) return 1;
+  for (const StreamJob& j : spread) printf("spread job n=%d k=%d wg0=%d wgn=%d rr=%d\n", j.n, j.k, j.wg0, j.wgn, j.rr);
   int cases = 0;
   for (int it = 0; it < 3000; ++it) {
     const int G = 1 + rnd(320);

@@ -231,6 +231,31 @@ def test_odd_shapes_step(M, T):
     p.close()
 
 
+# A stage whose matrices stay spread over the whole grid at M = 1: giving
+# them their own runs of workgroups would leave the largest share above
+# 33/32 of the even split's (on 256 workgroups).  The first matrix's 235
+# extra rows end at workgroup 235, where the 300-row matrix's extra rows
+# start, wrapping past the last workgroup to the first ones.
+EVEN_ROTATED = [(491, 1024, 0), (768, 1024, 0), (300, 64, 0), (129, 1024, 1)]
+
+
+def test_step_stage_spread_over_grid():
+    print("[case] rotated even split M=1", flush=True)
+    p, host, ys, lm, lmhost = build(1, 1, EVEN_ROTATED, (500, 1024), 38000)
+    p.run_persistent()
+    torch.cuda.synchronize()
+    assert p.check() == 0
+    check_outputs(1, 1, host, ys, lm, lmhost, "rotated even split M=1")
+    first = snapshot(ys, lm)
+    for sched in (p.run_unfused, p.run):
+        for y in ys:
+            y.fill_(float("nan"))
+        sched()
+        torch.cuda.synchronize()
+        assert same(first, snapshot(ys, lm)), sched.__name__
+    p.close()
+
+
 WIDE = [(640, 1024, 0), (64, 1024, 0), (1000, 1024, 0), (1, 1024, 0), (300, 1024, 0), (128, 2048, 1),
         (2049, 1024, 2)]
 

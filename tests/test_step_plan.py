@@ -28,4 +28,9 @@ def test_step_row_plan(tmp_path):
     assert runs[:3] == [(0, 86), (86, 85), (171, 85)]
     assert runs[3] == (0, 256) and runs[6] == (0, 256) and runs[7] == (0, 256)
     assert runs[4:6] == [(0, 128), (128, 128)]
+    # the stage of tests/test_gpu_pass.py::test_step_stage_spread_over_grid:
+    # every matrix on the whole grid, the 300-row one's extra rows from
+    # workgroup 235 on, wrapping past the last workgroup
+    spread = [ln for ln in lines if ln.startswith("spread job")]
+    assert [ln.split("wg0=")[1] for ln in spread] == ["0 wgn=256 rr=235", "235 wgn=256 rr=0", "235 wgn=256 rr=44"]
     assert lines[-1] == "random cases ok: 3000"
