@@ -133,10 +133,11 @@ def test_bitwise_repeatable(m, n, k):
 def test_row_bits_independent_of_matrix_height(m, k):
     """A row's output bits do not depend on how many other rows the launch
     has: the first rows of a 5120-row matrix, launched alone as matrices of
-    256, 300 and 1000 rows, give the same bits.  At M = 1 the row split
-    then gives a workgroup 1-4 rows of a chunk instead of 20, so its waves
-    lay out one row per half-wave instead of two (the summation must not
-    change with the layout)."""
+    256, 300 and 1000 rows, give the same bits.  At M = 1 and K = 17408 or
+    2048 (the step kernel) the row split then gives a workgroup 1-4 rows of
+    a chunk instead of 20, so its waves lay out one row per half-wave
+    instead of two (the summation must not change with the layout); at
+    K = 5120 the single call takes the GEMV items, the last one partial."""
     print(f"[case] row bits vs matrix height M={m} K={k}", flush=True)
     rng = np.random.default_rng(9600 + m + k)
     wq, ws = synth.gen_weights(rng, 5120, k)
