@@ -1116,8 +1116,9 @@ __device__ __forceinline__ void run_item(const StreamJob& j, int item, int M, De
 }
 
 // Publish the workgroup's lm_head bests (M = 1: every wave's best; M >= 2:
-// every wave's per-lane bests reduced over the 16 lanes sharing rows --
-// waves that hold none publish nothing).
+// per row, the best of the four waves' tables, which hold each wave's
+// per-lane bests reduced over the 16 lanes sharing rows -- rows that no
+// wave holds publish nothing).  Every thread calls it (M >= 2: a barrier).
 template <int MT, class BestT>
 __device__ __forceinline__ void publish(StreamCtl* ctl, int M, BestT& best) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1129,15 +1130,22 @@ __device__ __forceinline__ void publish(StreamCtl* ctl, int M, BestT& best) {
     if (oi >= 0 && (i < 0 || better(ov, oi, v, i))) { v = ov; i = oi; }
     if (lane == 0) publish_best(ctl, 0, v, i);
   } else {
-    (void)w;
-    // this wave's table: one key per row m (0: the wave saw none); more
-    // rows than lanes at MT = 5
-    for (int m = lane; m < 16 * MT && m < M; m += kWave) {
-      const unsigned long long k = best.tab[m];
-      if (k != 0ull)
-        __hip_atomic_fetch_max(&ctl->keys[m][blockIdx.x % kKeySlots], k, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // the waves' tables (one key per row m, 0: the wave saw none) reduced
+    // by wave 0, one atomic per row and workgroup (the four waves' atomics
+    // on the same lines took 72 against 77 us for a 65,536-row head at
+    // M = 17); more rows than lanes at MT = 5
+    __syncthreads();
+    if (w == 0)
+      for (int m = lane; m < 16 * MT && m < M; m += kWave) {
+        unsigned long long k = 0;
+        for (int v = 0; v < kWaves; ++v) {
+          const unsigned long long t = best.tab[v * 16 * MT + m];
+          k = t > k ? t : k;
+        }
+        if (k != 0ull)
+          __hip_atomic_fetch_max(&ctl->keys[m][blockIdx.x % kKeySlots], k, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
   }
 }
 
@@ -1316,15 +1324,20 @@ __attribute__((amdgpu_waves_per_eu(MT == 1 && MODE == MODE_DIRECT && FMT == 0 ? 
       if (my_stage >= 0) signal_stage(a, my_stage);
     }
     if (a.has_lmhead) publish<MT>(ctl, a.M, best);
-    __threadfence();
+    // Counting out without cache fences, as the stage signals do: every
+    // wave waits until its own memory operations (stores, signals, key
+    // atomics) are acknowledged before the workgroup's exit count, and the
+    // last workgroup out reads the keys with agent-scope loads.  (Agent-
+    // scope fences here, one per workgroup, made the 248,320-row lm_head
+    // verify at M = 17 take 297 instead of 240 us.)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (threadIdx.x == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(&ctl->exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned prev = __hip_atomic_fetch_add(&ctl->exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       lds_flag = prev == gridDim.x - 1;
     }
     __syncthreads();
     if (!lds_flag) return;
-    __threadfence();
     finish_lmhead(ctl, a, lds_am, lds_dep);
   }
 }
