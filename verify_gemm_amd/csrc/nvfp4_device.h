@@ -167,6 +167,15 @@ __device__ __forceinline__ void dma16(u32x4 rs, unsigned voff, unsigned lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m)
                : "memory", "m0");
 }
+// dma16 at device scope (sc1): each dword is read as an agent-scope relaxed
+// atomic load reads it (past the XCD's non-coherent L2), so data that
+// another workgroup wrote and acknowledged before a counter this wave has
+// seen is read fresh without an acquire fence.
+__device__ __forceinline__ void dma16_agent(u32x4 rs, unsigned voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen sc1 lds" ::"v"(voff), "s"(rs), "s"(m)
+               : "memory", "m0");
+}
 
 // s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt bits 3:0
 // and 15:14; expcnt 7 and lgkmcnt 15 = no wait on those).
