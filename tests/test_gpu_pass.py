@@ -256,6 +256,67 @@ def test_step_stage_spread_over_grid():
     p.close()
 
 
+def _selection_weights(n, k, rng):
+    """NVFP4 weights [n][k] whose row r is 1.0 at one column col[r] (E2M1
+    code 2; every E4M3 block scale 1.0, 0x38) and 0 elsewhere: with gscale
+    1, Y[m][r] = X[m][col[r]] exactly."""
+    col = rng.permutation(k)[:n]
+    wq = np.zeros((n, k // 2), np.uint8)
+    for r, c in enumerate(col):
+        wq[r, c // 2] = 2 if c % 2 == 0 else 2 << 4   # element 2j: the low nibble of byte j
+    ws = np.full((n, k // 16), 0x38, np.uint8)
+    return wq, ws, col
+
+
+def _as_activations(x_bits, col):
+    """The bf16 row that Y[m][r] = x[m][col[r]] (fp32, little-endian) reads
+    as: each float's low half (zero: x is bf16) then its high half."""
+    out = np.zeros((x_bits.shape[0], 2 * len(col)), np.uint16)
+    out[:, 1::2] = x_bits[:, col]
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 17])
+def test_stage_reads_what_an_earlier_stage_wrote(M):
+    """The stage contract with aliasing: stage 0 writes a buffer whose bytes
+    stage 1 reads as its activations; stage 2 writes the same buffer again
+    from other inputs and stage 3 reads it -- in one launch at M = 1, and
+    in every schedule.  A stage that read a stale copy of the buffer (what
+    stage 0 wrote, still cached from stage 1) would give stage 3 stage 1's
+    results."""
+    print(f"[case] chained stages through one buffer M={M}", flush=True)
+    rng = np.random.default_rng(39000 + M)
+    k0, k1, n1 = 1024, 2048, 300
+    wsel, ssel, col = _selection_weights(k1 // 2, k0, rng)
+    xs = []
+    for _ in range(2):
+        x = synth.gen_x(rng, M, k0)
+        x[(x & 0x7FFF) == 0] = 0x3F80                 # no signed zeros: 0 + (-0) would read back as +0
+        xs.append(x)
+    w1, s1 = synth.gen_weights(rng, n1, k1)
+    g1 = 0.75
+    buf = torch.full((M, k1 // 2), float("nan"), dtype=torch.float32, device="cuda")
+    xbuf = buf.view(torch.bfloat16)                   # [M][k1]: the same bytes
+    y1 = torch.empty((M, n1), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((M, n1), dtype=torch.float32, device="cuda")
+    sel_q, sel_s, q1, sc1 = dev_u8(wsel), dev_u8(ssel), dev_u8(w1), dev_u8(s1)
+    gemms = [(dev_bf16(xs[0]), sel_q, sel_s, 1.0, buf, 0), (xbuf, q1, sc1, g1, y1, 1),
+             (dev_bf16(xs[1]), sel_q, sel_s, 1.0, buf, 2), (xbuf, q1, sc1, g1, y2, 3)]
+    p = binding.Pass(gemms, M, None)
+    refs = [oracle.nvfp4_gemm_ref(_as_activations(x, col), w1, s1, g1) for x in xs]
+    for sched in (p.run, p.run_persistent, p.run_staged, p.run_unfused):
+        for y in (y1, y2):
+            y.fill_(float("nan"))
+        sched()
+        torch.cuda.synchronize()
+        assert p.check() == 0
+        assert np.array_equal(xbuf.cpu().view(torch.int16).numpy().view(np.uint16), _as_activations(xs[1], col))
+        for y, (y_ref, bound), name in ((y1, refs[0], "stage 1"), (y2, refs[1], "stage 3")):
+            ok, worst, at = within_bound(y.cpu().numpy(), y_ref, bound)
+            assert ok, f"{sched.__name__} {name}: worst err/bound {worst:.3g} at {at}"
+    p.close()
+
+
 WIDE = [(640, 1024, 0), (64, 1024, 0), (1000, 1024, 0), (1, 1024, 0), (300, 1024, 0), (128, 2048, 1),
         (2049, 1024, 2)]
 
